@@ -1,0 +1,415 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: the pages'
+matrix form of the gated delta rule evaluated in float64, closed forms of the
+scale rules, textbook quantisers, IEEE conversions from numpy, brute-force
+spectral norms, invariants the pages state, and an independent bit packer.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from quantized_delta_rule_decode_amd import synth
+
+D = 128
+RNG = np.random.default_rng
+
+
+def unit(x):
+    return x / np.linalg.norm(x)
+
+
+def f32(x):
+    return np.asarray(x, np.float32)
+
+
+def head_fp32(d, S):
+    """Decoded FP32-kind head holding the fp32 matrix S."""
+    kinds = np.full(d, 32, np.uint8)
+    e = f32(S).view(np.uint32).copy()
+    return kinds, e, np.zeros(d, np.float32), np.ones(d, np.float32)
+
+
+def matrix_delta_rule(S_prev, k, v, beta, a):
+    """Tutorial §二: S_t = (I - beta k k^T) D S_{t-1} + beta k v^T (float64)."""
+    d = S_prev.shape[0]
+    k = np.asarray(k, np.float64)
+    A = (np.eye(d) - beta * np.outer(k, k)) @ np.diag(np.asarray(a, np.float64))
+    return A @ np.asarray(S_prev, np.float64) + beta * np.outer(k, np.asarray(v, np.float64))
+
+
+# ------------------------------------------------------------------ fp16
+def test_fp16_matches_ieee(orc):
+    g = RNG(1)
+    vals = np.concatenate([
+        g.standard_normal(4000) * 10.0 ** g.uniform(-9, 5, 4000),
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e10, -1e10, 2 ** -24, 2 ** -25,
+         3 * 2 ** -26, 2 ** -25 + 2 ** -40, 6.1e-5, 2 ** -14, 2 ** -14 - 2 ** -25,
+         1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, float("inf"), -float("inf")],
+    ]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f32_to_f16(float(x)) for x in vals], np.uint16)
+    assert np.array_equal(got, ref)
+    back = np.array([orc.f16_to_f32(int(h)) for h in ref], np.float32)
+    assert np.array_equal(back, ref.view(np.float16).astype(np.float32))
+
+
+# ------------------------------------------------------------------ fold sum
+@pytest.mark.parametrize("n", [1, 2, 8, 128])
+def test_fold_sum_accuracy(orc, n):
+    x = RNG(n).standard_normal(n).astype(np.float32)
+    s = orc.fold_sum(x)
+    exact = math.fsum(map(float, x))
+    bound = math.ceil(math.log2(max(n, 2))) * 2 ** -24 * float(np.abs(x).astype(np.float64).sum())
+    assert abs(s - exact) <= bound + 1e-30
+    ints = np.arange(n, dtype=np.float32)
+    assert orc.fold_sum(ints) == n * (n - 1) / 2
+
+
+# ------------------------------------------------------------------ delta rule
+@pytest.mark.parametrize("d", [4, 16, 128])
+def test_delta_rule_matches_matrix_form(orc, d):
+    g = RNG(10 + d)
+    S0 = g.standard_normal((d, d)).astype(np.float32)
+    k = f32(unit(g.standard_normal(d)))
+    v = f32(g.standard_normal(d))
+    q = f32(unit(g.standard_normal(d)))
+    beta = float(np.float32(g.uniform()))
+    a = f32(g.uniform(0.5, 1.0, d))          # diagonal (KDA) gate
+    kinds, e, r, c = head_fp32(d, S0)
+    _, _, _, o, S_pre = orc.head_step(kinds, e, r, c, np.ones(d), q, k, v, beta, a)
+    ref = matrix_delta_rule(S0, k, v, beta, a)
+    assert np.max(np.abs(S_pre - ref)) <= 1e-5 * np.max(np.abs(ref))
+    o_ref = ref.T @ q.astype(np.float64)
+    assert np.linalg.norm(o - o_ref) <= 1e-5 * np.linalg.norm(o_ref)
+    # scalar (GDN) gate: same equation with D = alpha I
+    alpha = np.full(d, np.float32(0.9), np.float32)
+    _, _, _, _, S_pre = orc.head_step(kinds, e, r, c, np.ones(d), q, k, v, beta, alpha)
+    ref = matrix_delta_rule(S0, k, v, beta, alpha)
+    assert np.max(np.abs(S_pre - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_key_projection_is_column_sum(orc):
+    g = RNG(3)
+    Sp = g.standard_normal((D, D)).astype(np.float32)
+    k = f32(unit(g.standard_normal(D)))
+    v = f32(g.standard_normal(D))
+    _, u = orc.delta_update(Sp, k, v, 0.5)
+    ref = Sp.astype(np.float64).T @ k.astype(np.float64)
+    assert np.max(np.abs(u - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_unit_key_beta_one_writes_value(orc):
+    """With ||k|| = 1 and beta = 1 the update gives k^T S_t = v^T."""
+    g = RNG(4)
+    for kind in (32, 16, 8, 6):
+        S0 = g.standard_normal((D, D)).astype(np.float32)
+        kinds = np.full(D, kind, np.uint8)
+        e, r, c, _ = orc.requant(kinds, S0, np.ones(D))
+        k = unit(g.standard_normal(D))
+        v = g.standard_normal(D)
+        a = np.full(D, np.float32(0.8), np.float32)
+        _, _, _, _, S_pre = orc.head_step(kinds, e, r, c, np.ones(D), f32(unit(g.standard_normal(D))),
+                                          f32(k), f32(v), 1.0, a)
+        kt = f32(k).astype(np.float64)
+        kS = kt @ S_pre.astype(np.float64)
+        # exact identity up to fp32 rounding of S and of the unit-norm key
+        assert np.max(np.abs(kS - f32(v))) <= 1e-4 * (1 + np.max(np.abs(v)))
+
+
+def test_basis_key_rewrites_one_row(orc):
+    """k = e_m: row m becomes v (one rounding), every other row is D S' bit-exactly."""
+    g = RNG(5)
+    m = 37
+    k = np.zeros(D, np.float32)
+    k[m] = 1.0
+    for kind in (32, 8, 6, 4):
+        S0 = g.standard_normal((D, D)).astype(np.float32)
+        kinds = np.full(D, kind, np.uint8)
+        e, r, c, _ = orc.requant(kinds, S0, g.lognormal(0, 1, D).astype(np.float32))
+        a = f32(g.uniform(0.3, 1.0, D))
+        v = f32(g.standard_normal(D))
+        Sp = orc.dequant(kinds, e, r, c, a)
+        _, _, _, _, S_pre = orc.head_step(kinds, e, r, c, np.ones(D), k, k, v, 1.0, a)
+        others = np.arange(D) != m
+        assert np.array_equal(S_pre[others].view(np.uint32), Sp[others].view(np.uint32))
+        assert np.max(np.abs(S_pre[m] - v)) <= 2 ** -23 * np.max(np.abs(v)) * 2
+
+
+def test_transition_norm_bounded(orc):
+    """Tutorial §二: ||A_t||_2 <= ||D_t||_2 <= 1 for ||k|| <= 1, 0 <= beta <= 1, 0 <= D <= I.
+
+    A_t is assembled from the oracle itself: with S_{t-1} = I and v = 0 the
+    updated state is A_t.  The spectral norm is brute-forced by numpy's SVD.
+    """
+    g = RNG(6)
+    for d in (2, 4, 8):
+        for _ in range(200):
+            k = g.standard_normal(d)
+            k = k / np.linalg.norm(k) * g.uniform(0.2, 1.0)
+            beta = g.uniform()
+            a = g.uniform(0.0, 1.0, d)
+            kinds, e, r, c = head_fp32(d, np.eye(d))
+            _, _, _, _, A = orc.head_step(kinds, e, r, c, np.ones(d), np.zeros(d, np.float32),
+                                          f32(k), np.zeros(d, np.float32), beta, f32(a))
+            nA = np.linalg.norm(A.astype(np.float64), 2)
+            nD = np.max(np.abs(f32(a)))
+            assert nA <= nD * (1 + 1e-6) + 1e-7 and nD <= 1.0
+            # the delta factor only damps the key direction (D = I case)
+        kinds, e, r, c = head_fp32(d, np.eye(d))
+        k = f32(unit(g.standard_normal(d)))
+        _, _, _, _, A = orc.head_step(kinds, e, r, c, np.ones(d), np.zeros(d, np.float32), k,
+                                      np.zeros(d, np.float32), 0.5, np.ones(d, np.float32))
+        A = A.astype(np.float64)
+        assert np.allclose(A @ k, 0.5 * k, atol=1e-6)
+        x = g.standard_normal(d)
+        x -= (x @ k) * k
+        assert np.allclose(A @ x, x, atol=1e-6)
+
+
+def test_readout_is_state_transpose_query(orc):
+    g = RNG(7)
+    S = g.standard_normal((D, D)).astype(np.float32)
+    for m in (0, 5, 127):
+        q = np.zeros(D, np.float32)
+        q[m] = 1.0
+        assert np.array_equal(orc.readout(S, q), S[m])
+    q = f32(g.standard_normal(D))
+    o = orc.readout(S, q)
+    ref = S.astype(np.float64).T @ q.astype(np.float64)
+    assert np.max(np.abs(o - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ unquantised modes
+def test_fp32_trajectory_matches_float64(orc):
+    """FP32 kind reproduces the plain delta rule (float64 reference, 64 steps)."""
+    g = RNG(8)
+    d = D
+    S64 = np.zeros((d, d))
+    kinds, e, r, c = head_fp32(d, np.zeros((d, d)))
+    for t in range(64):
+        k = unit(g.standard_normal(d))
+        v = g.standard_normal(d)
+        q = unit(g.standard_normal(d)) / math.sqrt(d)
+        beta = g.uniform()
+        alpha = math.exp(-g.uniform(1e-4, 0.5))
+        k32, v32, q32 = f32(k), f32(v), f32(q)
+        b32, a32 = float(np.float32(beta)), np.full(d, np.float32(alpha), np.float32)
+        e, r, c, o, _ = orc.head_step(kinds, e, r, c, np.ones(d), q32, k32, v32, b32, a32)
+        S64 = matrix_delta_rule(S64, k32, v32, b32, a32)
+        o64 = S64.T @ q32.astype(np.float64)
+        assert np.linalg.norm(o - o64) <= 1e-5 * np.linalg.norm(o64)
+    S = e.view(np.float32)
+    assert np.linalg.norm(S - S64) <= 1e-5 * np.linalg.norm(S64)
+
+
+def test_fp16_trajectory_tracks_fp32(orc):
+    g = RNG(9)
+    d = D
+    k16 = np.full(d, 16, np.uint8)
+    e16, r, c, _ = orc.requant(k16, np.zeros((d, d), np.float32), np.ones(d))
+    kinds32, e32, r32, c32 = head_fp32(d, np.zeros((d, d)))
+    for t in range(64):
+        k = f32(unit(g.standard_normal(d)))
+        v = f32(g.standard_normal(d))
+        q = f32(unit(g.standard_normal(d)) / math.sqrt(d))
+        beta = float(np.float32(g.uniform()))
+        a = np.full(d, np.float32(math.exp(-g.uniform(1e-4, 0.5))), np.float32)
+        e16, r, c, o16, _ = orc.head_step(k16, e16, r, c, np.ones(d), q, k, v, beta, a)
+        e32, r32, c32, o32, _ = orc.head_step(kinds32, e32, r32, c32, np.ones(d), q, k, v, beta, a)
+        assert np.linalg.norm(o16 - o32) <= 5e-3 * np.linalg.norm(o32)
+    S16 = orc.dequant(k16, e16, r, c, np.ones(d, np.float32))
+    S32 = e32.view(np.float32)
+    assert np.linalg.norm(S16 - S32) <= 5e-3 * np.linalg.norm(S32)
+
+
+# ------------------------------------------------------------------ scales and codes
+def _dual_reference(S, omega, kinds):
+    """Float64 evaluation of the dual-axis rules with the oracle's fp32 factors."""
+    S64 = S.astype(np.float64)
+    m = np.abs(S64).mean(axis=1)
+    r = np.sqrt(m / omega.astype(np.float64))
+    return m, r
+
+
+@pytest.mark.parametrize("kind", [2, 4, 6, 8])
+def test_dual_axis_closed_forms(orc, kind):
+    g = RNG(20 + kind)
+    S = synth.random_state(20 + kind, 1, 1)[0, 0]
+    omega = g.lognormal(0, 1, D).astype(np.float32)
+    kinds = np.full(D, kind, np.uint8)
+    e, r, c, m = orc.requant(kinds, S, omega)
+    z = e.view(np.int32)
+    qmax = 2 ** (kind - 1) - 1
+    m64, r64 = _dual_reference(S, omega, kinds)
+    assert np.max(np.abs(m - m64) / m64) <= 1e-6          # mean |S_ij| over the row
+    assert np.max(np.abs(r - r64) / r64) <= 1e-6          # r = m^(1/2) w^(-1/2)
+    c64 = np.max(np.abs(S.astype(np.float64) / r.astype(np.float64)[:, None]), axis=0)
+    assert np.max(np.abs(c - c64) / c64) <= 1e-6          # clip-free column range
+    assert np.all(np.abs(z) <= qmax)
+    # the reconstruction error of every element is within half a grid step
+    X = r.astype(np.float64)[:, None] * c.astype(np.float64)[None, :] * z / qmax
+    step = r.astype(np.float64)[:, None] * c.astype(np.float64)[None, :] / qmax
+    assert np.all(np.abs(X - S) <= 0.5 * step * (1 + 1e-5))
+    # codes equal the float64 rounding except at exact-tie neighbourhoods
+    t = S.astype(np.float64) / (r.astype(np.float64)[:, None] * c.astype(np.float64)[None, :]) * qmax
+    near_tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-5
+    assert np.array_equal(z[~near_tie], np.rint(t[~near_tie]).astype(np.int32))
+    # the column maximum is attained: some row reaches the full code range
+    assert np.all(np.max(np.abs(z), axis=0) == qmax)
+
+
+def test_row_absmax_is_uniform_int8(orc):
+    """Baseline quantiser: symmetric INT8 with a per-key-row absmax scale."""
+    S = synth.random_state(31, 1, 1)[0, 0]
+    kinds = np.full(D, 8, np.uint8)
+    e, r, c, _ = orc.requant(kinds, S, np.ones(D), scale_mode=1)
+    z = e.view(np.int32)
+    absmax = np.max(np.abs(S), axis=1).astype(np.float64)
+    assert np.array_equal(r, absmax.astype(np.float32))
+    t = S.astype(np.float64) / (absmax[:, None] / 127.0)
+    ref = np.rint(t)
+    near_tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-4
+    assert np.array_equal(z[~near_tie], ref[~near_tie].astype(np.int32))
+    assert np.count_nonzero(z != ref) <= 1e-3 * z.size
+    assert np.all(np.abs(z) <= 127) and np.all(np.max(np.abs(z), axis=1) == 127)
+    # dequantised values: z * absmax / 127
+    X = orc.dequant(kinds, e, r, c, np.ones(D, np.float32))
+    assert np.max(np.abs(X - S) / absmax[:, None]) <= 0.5 / 127 * (1 + 1e-5)
+
+
+def test_power_of_four_scaling_is_exact(orc):
+    """S x4 and v x4 give identical codes, r x2, c x2 and o x4 bit-exactly."""
+    g = RNG(40)
+    S = synth.random_state(40, 1, 1)[0, 0]
+    omega = g.lognormal(0, 1, D).astype(np.float32)
+    for kinds in (np.full(D, 6, np.uint8), np.array([8, 6, 4, 2] * 32, np.uint8)):
+        e, r, c, _ = orc.requant(kinds, S, omega)
+        e4, r4, c4, _ = orc.requant(kinds, S * np.float32(4), omega)
+        assert np.array_equal(e, e4)
+        assert np.array_equal(r * 2, r4) and np.array_equal(c * 2, c4)
+        q = f32(unit(g.standard_normal(D)))
+        k = f32(unit(g.standard_normal(D)))
+        v = f32(g.standard_normal(D))
+        a = f32(g.uniform(0.5, 1, D))
+        s1 = orc.head_step(kinds, e, r, c, omega, q, k, v, 0.7, a)
+        s4 = orc.head_step(kinds, e4, r4, c4, omega, q, k, v * np.float32(4), 0.7, a)
+        assert np.array_equal(s1[0], s4[0])
+        assert np.array_equal(s1[1] * 2, s4[1]) and np.array_equal(s1[2] * 2, s4[2])
+        assert np.array_equal(s1[3] * 4, s4[3])
+
+
+def test_weighted_column_refit(orc):
+    """V1a: the refit column factor is the weighted least-squares optimum for the codes."""
+    g = RNG(50)
+    S = synth.random_state(50, 1, 1)[0, 0]
+    omega = g.lognormal(0, 1, D).astype(np.float32)
+    kinds = np.array([8, 6, 4, 2] * 32, np.uint8)
+    e0, r0, c0, m = orc.requant(kinds, S, omega, fit_iters=0)
+    e1, r1, c1, _ = orc.requant(kinds, S, omega, fit_iters=1)
+    assert np.array_equal(e0, e1) and np.array_equal(r0, r1)
+    z = e1.view(np.int32).astype(np.float64)
+    qmax = (2.0 ** (kinds.astype(np.float64) - 1) - 1)[:, None]
+    zeta = z / qmax
+    w = omega.astype(np.float64)[:, None]
+    rr = r1.astype(np.float64)[:, None]
+    S64 = S.astype(np.float64)
+    for j in range(D):
+        A = (np.sqrt(w[:, 0]) * rr[:, 0] * zeta[:, j])[:, None]
+        y = np.sqrt(w[:, 0]) * S64[:, j]
+        cstar = np.linalg.lstsq(A, y, rcond=None)[0][0]
+        assert abs(c1[j] - cstar) <= 1e-5 * abs(cstar)
+        err = lambda cj: float(np.sum(w[:, 0] * (S64[:, j] - rr[:, 0] * cj * zeta[:, j]) ** 2))
+        assert err(float(c1[j])) <= err(float(c0[j])) * (1 + 1e-9)
+
+
+def test_mixed_rows_share_column_factor(orc):
+    """Rows of any width use one column factor: X = r c z / q_i (reading of tutorial §四)."""
+    S = synth.random_state(60, 1, 1)[0, 0]
+    kinds = np.array([2, 4, 6, 8, 16, 32] * 21 + [8, 8], np.uint8)
+    omega = np.ones(D, np.float32)
+    e, r, c, _ = orc.requant(kinds, S, omega)
+    X = orc.dequant(kinds, e, r, c, np.ones(D, np.float32))
+    for i in range(D):
+        if kinds[i] == 32:
+            assert np.array_equal(X[i], S[i])
+        elif kinds[i] == 16:
+            assert np.array_equal(X[i], S[i].astype(np.float16).astype(np.float32))
+        else:
+            q = 2 ** (int(kinds[i]) - 1) - 1
+            step = float(r[i]) * c.astype(np.float64) / q
+            assert np.all(np.abs(X[i] - S[i]) <= 0.5 * step * (1 + 1e-5) + 1e-30)
+            assert r[i] > 0
+        if kinds[i] >= 16:
+            assert r[i] == 0
+
+
+def test_gate_scales_restored_rows(orc):
+    """Dequantisation with gate a equals a_i times the plain restored row."""
+    g = RNG(61)
+    S = synth.random_state(61, 1, 1)[0, 0]
+    kinds = np.array([8, 6, 4, 2, 16, 32, 6, 8] * 16, np.uint8)
+    e, r, c, _ = orc.requant(kinds, S, g.lognormal(0, 1, D).astype(np.float32))
+    a = f32(g.uniform(0, 1, D))
+    X1 = orc.dequant(kinds, e, r, c, np.ones(D, np.float32)).astype(np.float64)
+    Xa = orc.dequant(kinds, e, r, c, a).astype(np.float64)
+    assert np.max(np.abs(Xa - a[:, None] * X1) / (np.abs(X1) + 1e-30)) <= 3e-7
+
+
+# ------------------------------------------------------------------ invariants of the step
+def test_identity_step_leaves_state(orc):
+    """beta = 0, D = I: exact for FP32/FP16, codes kept for the row-absmax INT8 baseline."""
+    g = RNG(70)
+    S = synth.random_state(70, 1, 1)[0, 0]
+    ones = np.ones(D, np.float32)
+    zero = np.zeros(D, np.float32)
+    for kind, mode in ((32, 0), (16, 0), (8, 1)):
+        kinds = np.full(D, kind, np.uint8)
+        e, r, c, _ = orc.requant(kinds, S, ones, scale_mode=mode)
+        e2, r2, c2, _, _ = orc.head_step(kinds, e, r, c, ones, zero, f32(unit(g.standard_normal(D))),
+                                         f32(g.standard_normal(D)), 0.0, ones, scale_mode=mode)
+        assert np.array_equal(e, e2)
+        if kind == 8:
+            assert np.max(np.abs(r2 - r) / r) <= 2 ** -23
+    # dual-axis: state drifts by at most half a grid step of the new scales
+    omega = g.lognormal(0, 1, D).astype(np.float32)
+    kinds = np.full(D, 6, np.uint8)
+    e, r, c, _ = orc.requant(kinds, S, omega)
+    X = orc.dequant(kinds, e, r, c, ones)
+    e2, r2, c2, _, _ = orc.head_step(kinds, e, r, c, omega, zero, f32(unit(g.standard_normal(D))),
+                                     zero, 0.0, ones)
+    X2 = orc.dequant(kinds, e2, r2, c2, ones)
+    step = r2.astype(np.float64)[:, None] * c2.astype(np.float64)[None, :] / 31
+    assert np.all(np.abs(X2 - X) <= 0.5 * step * (1 + 1e-5))
+
+
+def test_error_recursion(orc):
+    """Tutorial §二: E_t = A_t E_{t-1} + eps_t for the quantised path vs the fp32 path."""
+    g = RNG(80)
+    d = D
+    omega = g.lognormal(0, 1, d).astype(np.float32)
+    kinds = np.full(d, 6, np.uint8)
+    S0 = synth.random_state(80, 1, 1)[0, 0]
+    e, r, c, _ = orc.requant(kinds, S0, omega)
+    X_prev = orc.dequant(kinds, e, r, c, np.ones(d, np.float32)).astype(np.float64)
+    S32 = X_prev.copy()           # fp32 reference path starts from the same state
+    for t in range(16):
+        k = f32(unit(g.standard_normal(d)))
+        v = f32(g.standard_normal(d))
+        q = f32(unit(g.standard_normal(d)) / math.sqrt(d))
+        beta = float(np.float32(g.uniform()))
+        a = np.full(d, np.float32(math.exp(-g.uniform(1e-4, 0.5))), np.float32)
+        E_prev = X_prev - S32
+        e, r, c, o, S_pre = orc.head_step(kinds, e, r, c, omega, q, k, v, beta, a)
+        A = (np.eye(d) - beta * np.outer(k, k)) @ np.diag(a.astype(np.float64))
+        S32 = A @ S32 + beta * np.outer(k, v)
+        X = orc.dequant(kinds, e, r, c, np.ones(d, np.float32)).astype(np.float64)
+        eps = X - S_pre                        # error injected by this step's requantisation
+        E = X - S32
+        lhs = E - (A @ E_prev + eps)
+        assert np.max(np.abs(lhs)) <= 1e-5 * np.max(np.abs(S32))
+        # the readout used the state before requantisation
+        assert np.linalg.norm(o - S_pre.astype(np.float64).T @ q) <= 1e-6 * np.linalg.norm(o)
+        X_prev = X

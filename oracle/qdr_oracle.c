@@ -290,7 +290,7 @@ void or_head_step(int d, const uint8_t *kinds, uint32_t *e, float *r,
 /*  - the code stream of column j holds rows 0..127 in order, row i as a     */
 /*    field of b_i bits (b = 2,4,6,8 integer codes, 16 binary16, 32          */
 /*    binary32); stream bit p is bit p%8 of stream byte p/8;                 */
-/*  - integer codes are stored offset-binary: field = z + 2^(b-1);           */
+/*  - integer codes are stored as b-bit two's complement;                    */
 /*  - the stream is cut into granules of G bytes (G = 16 for whole-head      */
 /*    units, 4 for row units), zero-padded to whole granules; granule g of   */
 /*    column j sits at byte (g*128 + j)*G of the block;                      */
@@ -331,10 +331,7 @@ static size_t stream_byte(int unit, int j, size_t n) {
 }
 
 static uint32_t field_of(int kind, uint32_t e) {
-  if (kind_is_int(kind)) {
-    int32_t z = (int32_t)e;
-    return (uint32_t)(z + (1 << (kind - 1)));
-  }
+  if (kind_is_int(kind)) return e & ((1u << kind) - 1u);   /* low b bits of z */
   return e;   /* FP16 bits or FP32 bits */
 }
 
@@ -369,8 +366,8 @@ void or_decode_block(const uint8_t *kinds, int unit, int scale_mode,
       uint32_t f = 0;
       for (int t = 0; t < w; ++t, ++p)
         if ((block[stream_byte(unit, j, p / 8)] >> (p % 8)) & 1u) f |= 1u << t;
-      if (kind_is_int(kinds[i]))
-        e[i * D128 + j] = (uint32_t)((int32_t)f - (1 << (w - 1)));
+      if (kind_is_int(kinds[i]))   /* sign-extend the b-bit field */
+        e[i * D128 + j] = (f & (1u << (w - 1))) ? (f | ~((1u << w) - 1u)) : f;
       else
         e[i * D128 + j] = f;
     }

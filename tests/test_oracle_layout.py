@@ -28,7 +28,7 @@ def ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c):
         pos = 0
         for i, w in enumerate(widths):
             if w <= 8:
-                field = int(codes[i, j]) + (1 << (w - 1))
+                field = int(codes[i, j]) % (1 << w)     # b-bit two's complement
             else:
                 field = int(fp_bits[i, j])
             assert 0 <= field < (1 << w)

@@ -1,0 +1,162 @@
+"""Benchmark of the fused quantized delta-rule decode step on one MI355X.
+
+Workload (default): the full GDN pool -- B = 512 requests x 2304 heads of
+128 x 128 states, nominal 6-bit (46 FP16 pivot heads, 691 INT8, 991 INT6,
+576 INT4; mean 6.30 code bits), dual-axis scales, warm state from 256 FP32
+delta-rule steps, about 15 GB of packed codes resident in HBM.  One "step" is
+one qdr_decode_step over the whole pool: every (request, head) state is
+restored, updated, read out, refitted, requantised and written back.
+
+Prints one JSON line: state-update steps/s (requests x heads) and achieved HBM
+GB/s from the algorithmic bytes, the roofline block, and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "state-update steps/s (requests x heads) at B=512, 6-bit; achieved HBM GB/s"
+
+
+def algorithmic_bytes(cfg, pool, kinds_per_head) -> int:
+    """Bytes the step must move, per the method: codes and scales read and
+    written once, q/k/v read, beta and the gate read, o written."""
+    H = cfg.H
+    per_req = 0
+    for h in range(H):
+        code = int(pool.code_bytes[h])
+        scales = 0
+        if kinds_per_head[h] <= 8:
+            scales = 2 * 128 * 4 if cfg.scale_mode == 0 else 128 * 4
+        per_req += 2 * code + 2 * scales
+    gate_bytes = 4 if cfg.gate == 0 else 4 * 128
+    per_req += H * (3 * 128 * 4 + 4 + gate_bytes + 128 * 4)
+    return per_req * cfg.B
+
+
+def cpu_baseline(cfg, tables, requests: int, threads: int):
+    """The CPU oracle, as it stands, on `requests` requests x all heads."""
+    from oracle import oracle as orc
+    from quantized_delta_rule_decode_amd import synth
+    P = orc.Pool(requests, cfg.H, tables["kinds"], tables["omega"], unit=cfg.unit,
+                 gate=cfg.gate, scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters).alloc()
+    slots = np.arange(requests, dtype=np.int32)
+    P.pack(slots, synth.random_state(77, requests, cfg.H), threads=threads)
+    sub = synth.Config(**{**cfg.__dict__, "B": requests, "device_inputs": False})
+    ins = synth.step_inputs(sub, tables, 0)
+    t0 = time.perf_counter()
+    P.step(slots, *ins, threads=threads)
+    dt = time.perf_counter() - t0
+    return requests * cfg.H / dt, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--fp32-warmup-steps", type=int, default=None,
+                    help="FP32 delta-rule steps that build the warm state (default: the config's)")
+    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step has no "
+              "cross-GPU term, see the sharding paragraph of DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_delta_rule_decode_amd import qdr, synth, workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.CONFIGS[args.config]
+    tables = synth.static_tables(cfg)
+    dev = torch.device("cuda")
+    t_setup = time.perf_counter()
+    pool = workload.make_pool(cfg, tables)
+    slots = torch.from_numpy(tables["slots"]).to(dev)
+    warm = cfg.warmup if args.fp32_warmup_steps is None else args.fp32_warmup_steps
+    if warm > 0:
+        f32 = workload.warm_start(cfg, tables, pool, slots, warm)
+        f32.close()
+        del f32
+    else:
+        pool.qdr_slot_reset(slots)
+    q, k, v, beta, gate = workload.step_inputs(cfg, tables, 0, device=dev)
+    o = torch.empty((cfg.B, cfg.H, 128), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pool.qdr_decode_step(slots, q, k, v, beta, gate, o)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pool.qdr_decode_step(slots, q, k, v, beta, gate, o)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    assert pool.qdr_poll_device_error() == 0
+
+    kinds_h = tables["kinds"] if cfg.unit == 0 else None
+    if kinds_h is None:
+        kinds_h = np.full(cfg.H, 4, np.uint8)
+    nbytes = algorithmic_bytes(cfg, pool, kinds_h)
+    head_steps = cfg.B * cfg.H
+    achieved = nbytes / (gpu_ms * 1e-3) / 1e9
+    value = head_steps / (gpu_ms * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(os.cpu_count() or 1, 16)
+        rate, dt = cpu_baseline(cfg, tables, args.cpu_requests, threads)
+        cpu = {"value": rate, "unit": "state-update steps/s", "cores": threads, "kind": "oracle",
+               "sample": f"{args.cpu_requests} requests x {cfg.H} heads, one step ({dt:.2f} s)"}
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "state-update steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": gpu_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.H, "d_k": 128, "d_v": 128,
+                   "mean_code_bits": round(float(np.mean(tables["kinds"])), 3),
+                   "stored_bits_per_value": round(pool.bits_per_value, 3),
+                   "fp32_warmup_steps": warm},
+        "achieved_GBps": achieved,
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None},
+        "cpu_baseline": cpu,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "setup_s": setup_s,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

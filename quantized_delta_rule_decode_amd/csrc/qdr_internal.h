@@ -1,0 +1,56 @@
+// qdr_internal.h -- structures shared by the host runtime and the HIP kernels
+// of libqdr (never installed; the public ABI is include/qdr.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace qdr {
+
+constexpr int kDim = 128;
+
+enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3 };
+
+// Per-head metadata on the device (16 bytes).
+struct HeadInfo {
+  uint64_t off;         // block offset inside a slot
+  uint32_t code_bytes;  // bytes of the code region
+  uint16_t words;       // row units: 32-bit words per column stream
+  uint8_t kind;         // whole-head units: the head's kind; row units: 0
+  uint8_t has_scales;   // 1 when the block stores r (and c)
+};
+
+// Everything a launch needs, passed by value as the kernel argument.
+struct LaunchArgs {
+  uint8_t *pool;
+  uint64_t slot_stride;
+  int32_t num_slots;
+  int32_t H;
+  const HeadInfo *heads;
+  const int32_t *head_list;   // heads handled by this launch
+  int32_t n_list;
+  const uint8_t *row_kind;    // [H*128] (row units)
+  const uint16_t *row_bit;    // [H*128] bit offset of row i in a column stream
+  const float *omega;         // [H*128]
+  uint32_t *err;              // device error word
+  const int32_t *slots;       // [n] slot of each request / dense entry
+  const float *q, *k, *v, *beta, *gate;
+  float *o;
+  const float *S_in;          // pack: [n][H][128][128]
+  float *S_out;               // unpack
+};
+
+struct PoolConfig {
+  int unit, gate, scale_mode, fit_iters;
+  int max_words;              // row units: largest words-per-column of any head
+};
+
+// Launch every kernel of one mode over `n` requests / dense entries.
+// Returns hipSuccess or the first launch error.
+hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n,
+                      const int32_t *const *kind_lists, const int32_t *kind_counts,
+                      int mode, hipStream_t stream);
+
+}  // namespace qdr

@@ -1,0 +1,561 @@
+// qdr_kernels.hip -- CDNA4 (gfx950) kernels of the quantized gated delta-rule
+// decode step.
+//
+// One workgroup of 128 threads (two wave64s) owns one (request, head) 128x128
+// state.  Wave w holds key rows 64w..64w+63; lane l holds value columns l and
+// l+64 of those rows, so the whole fp32 tile lives in 128 VGPRs per lane:
+//   * column sums (u = S'^T k, o = S^T q, the column maximum of the scale fit)
+//     are lane-local fma chains;
+//   * row sums (the row magnitude m_i) are a lane-local pair add followed by a
+//     transpose-reduce: v_permlane32_swap, v_permlane16_swap, then one LDS
+//     hop for the last sixteen partials;
+//   * every per-row scalar (gate * row factor, k_i, beta*k_i, q_i, 1/r_i) is
+//     broadcast from LDS, so VALU instructions never exceed the one-SGPR limit.
+// Codes stream in and out as 16-byte granules laid out so that one wave
+// instruction touches 1 KiB of consecutive bytes.
+//
+// Arithmetic order (must match the written specification bit for bit):
+//   restore  rho_i = r_i / q_i, g_i = a_i * rho_i, S'_ij = (z_ij * g_i) * c_j
+//   update   u_j = fma chain over i ascending, delta_j = v_j - u_j,
+//            b_i = beta * k_i, S_ij = fma(b_i, delta_j, S'_ij)
+//   scales   m_i = foldsum_j |S_ij| * 2^-7, r_i = sqrt(m_i / omega_i) (1 if the
+//            quotient is 0), Y = S * (1/r_i), c0_j = max_i |Y_ij| (1 if below
+//            2^-126), z = nearest-even(Y * ((1/c0_j) * q)) of the exact product
+// Page references: gated delta rule and gate forms, tutorial
+// "STEPQuant：取代 KV cache 的状态，6-bit 量化精度不掉" §二; dual-axis factors,
+// pivots and the fused online kernel, same tutorial §四; restore / update /
+// read out / quantise order, review "STEPQuant：誤差の寿命と位置から設計する
+// Delta則の再帰状態量子化", generation-time paragraph.
+#include <float.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qdr_internal.h"
+
+namespace qdr {
+
+namespace {
+
+// 1.5 * 2^23: adding it to |x| < 2^22 leaves round-to-nearest-even(x) in the
+// low mantissa bits (two's complement), so fma(Y, w, kMagic) both rounds the
+// exact product Y*w and yields the code's bit pattern.
+constexpr float kMagic = 12582912.0f;
+
+template <int BITS>
+struct Kind {
+  static constexpr bool is_int = BITS <= 8;
+  static constexpr int qmax_i = is_int ? (1 << (BITS - 1)) - 1 : 0;
+  static constexpr int NG = BITS / 2;   // 16-byte granules per column half
+  static constexpr int NW = BITS * 2;   // 32-bit words per column half
+};
+
+__device__ __forceinline__ float rn_div(float a, float b) { return __fdiv_rn(a, b); }
+__device__ __forceinline__ float rn_sqrt(float a) { return __fsqrt_rn(a); }
+
+// b-bit field number `ii` of a column-half stream held in w[] (two's
+// complement for integer kinds, raw bits otherwise).
+template <int BITS>
+__device__ __forceinline__ uint32_t field_bits(const uint32_t *w, int ii) {
+  const int p = ii * BITS, d = p >> 5, s = p & 31;
+  if (BITS == 32) return w[d];
+  if (s + BITS <= 32) return w[d] >> s;
+  return __builtin_amdgcn_alignbit(w[d + 1], w[d], s);
+}
+
+template <int BITS>
+__device__ __forceinline__ float field_int_as_float(const uint32_t *w, int ii) {
+  const int p = ii * BITS, d = p >> 5, s = p & 31;
+  if (BITS == 8) return (float)(int)(int8_t)(uint8_t)(w[d] >> s);
+  int32_t x;
+  if (s + BITS <= 32)
+    x = __builtin_amdgcn_sbfe((int32_t)w[d], s, BITS);
+  else
+    x = __builtin_amdgcn_sbfe((int32_t)__builtin_amdgcn_alignbit(w[d + 1], w[d], s), 0, BITS);
+  return (float)x;
+}
+
+// Append field `ii` (low BITS bits of f) to the output stream: funnel shifts
+// bring the new bits in from the top, so bits above BITS never reach memory.
+template <int BITS>
+__device__ __forceinline__ void put_field(uint32_t *out, uint32_t &acc, uint32_t f, int ii) {
+  const int p = ii * BITS, d = p >> 5, s = p & 31;
+  if (BITS == 32) { out[d] = f; return; }
+  if (s + BITS < 32) {
+    acc = __builtin_amdgcn_alignbit(f, acc, BITS);
+  } else if (s + BITS == 32) {
+    acc = __builtin_amdgcn_alignbit(f, acc, BITS);
+    out[d] = acc;
+  } else {
+    acc = __builtin_amdgcn_alignbit(f, acc, 32 - s);
+    out[d] = acc;
+    acc = __builtin_amdgcn_alignbit(f, acc, BITS);
+  }
+}
+
+__device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// Row reduction of |S| over the 128 columns of each of this wave's 64 rows.
+// SUM: the fold-by-halves tree over the 128 columns (pairs j/j+64 are the
+// lane's own two columns; then j/j+32 by
+// permlane32_swap, j/j+16 by permlane16_swap, j/j+8 .. j/j+1 after one LDS
+// transpose).  MAX: the same tree with max.  Returns the value of row
+// 64w + lane.  red: this wave's [64][20] LDS scratch.
+template <bool MAX>
+__device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red)[20], int lane) {
+  // level j/j+64 is lane-local; it is formed pair by pair so that only the
+  // 32 level-two partials are live next to the tile
+  float q1[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const float p0 = MAX ? fmaxf(fabsf(S[0][2 * t]), fabsf(S[1][2 * t]))
+                         : fabsf(S[0][2 * t]) + fabsf(S[1][2 * t]);
+    const float p1 = MAX ? fmaxf(fabsf(S[0][2 * t + 1]), fabsf(S[1][2 * t + 1]))
+                         : fabsf(S[0][2 * t + 1]) + fabsf(S[1][2 * t + 1]);
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
+    q1[t] = MAX ? fmaxf(x, y) : x + y;
+  }
+  float q2[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(q1[2 * s]), __float_as_uint(q1[2 * s + 1]),
+                                               false, false);
+    const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
+    q2[s] = MAX ? fmaxf(x, y) : x + y;
+  }
+  // lane group G = lane/16 now holds rows 4s + {0,2,1,3}[G]; n = lane%16 is
+  // the column residue of the partial.
+  const int G = lane >> 4, n = lane & 15;
+  const int rsub = (G == 0) ? 0 : (G == 1) ? 2 : (G == 2) ? 1 : 3;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) red[4 * s + rsub][n] = q2[s];
+  __builtin_amdgcn_wave_barrier();
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 t = lds4(&red[lane][4 * i]);
+    x[4 * i + 0] = t.x; x[4 * i + 1] = t.y; x[4 * i + 2] = t.z; x[4 * i + 3] = t.w;
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int half = 8; half >= 1; half >>= 1) {
+#pragma unroll
+    for (int i = 0; i < half; ++i) x[i] = MAX ? fmaxf(x[i], x[i + half]) : x[i] + x[i + half];
+  }
+  return x[0];
+}
+
+// Restore this wave's 64 rows of both lane columns into S (gate included).
+template <int BITS>
+__device__ __forceinline__ void restore_rows(float (&S)[2][64], const uint32_t (&wd)[2][Kind<BITS>::NW],
+                                             const float (&colc)[2], const float *gsh, int row0) {
+#pragma unroll
+  for (int i4 = 0; i4 < 16; ++i4) {
+    const float4 g4 = lds4(&gsh[row0 + 4 * i4]);
+    const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ii = 4 * i4 + e;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float sp;
+        if (Kind<BITS>::is_int) {
+          const float zf = field_int_as_float<BITS>(wd[c], ii);
+          sp = (zf * gg[e]) * colc[c];
+        } else if (BITS == 16) {
+          sp = gg[e] * __half2float(__ushort_as_half((unsigned short)(field_bits<16>(wd[c], ii) & 0xFFFFu)));
+        } else {
+          sp = gg[e] * __uint_as_float(field_bits<32>(wd[c], ii));
+        }
+        S[c][ii] = sp;
+      }
+    }
+    // keep the scheduler from hoisting every extraction ahead of use, which
+    // would hold all 128 unpacked codes next to the tile
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Continue the key-projection chains u_c over this wave's 64 rows, in order.
+__device__ __forceinline__ void key_chain(const float (&S)[2][64], float (&u)[2], const float *ksh, int row0) {
+#pragma unroll
+  for (int i4 = 0; i4 < 16; ++i4) {
+    const float4 k4 = lds4(&ksh[row0 + 4 * i4]);
+    const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[0] = __builtin_fmaf(kk[e], S[0][4 * i4 + e], u[0]);
+      u[1] = __builtin_fmaf(kk[e], S[1][4 * i4 + e], u[1]);
+    }
+  }
+}
+
+struct Shared {
+  float g[kDim];     // restore factor a_i * r_i / q_i (or a_i for float kinds)
+  float k[kDim];
+  float b[kDim];     // beta * k_i
+  float q[kDim];
+  float ir[kDim];    // 1 / r_i
+  float m[kDim];     // row magnitude (refit weights)
+  float x[kDim];     // u hand-off, then o partial of wave 1
+  float d[kDim];     // delta, then refit numerator hand-off
+  float y[kDim];     // refit denominator hand-off
+  float cmax[2][kDim];
+  float red[2][64][20];
+};
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+// Whole-head kernel: every row of the head has kind BITS.
+// MODE_STEP: restore, gate, delta update, readout, requantise, store.
+// MODE_PACK: requantise S_in.  MODE_UNPACK: restore into S_out.
+// MODE_RESET: requantise S = 0.
+// --------------------------------------------------------------------------
+template <int BITS, int MODE, int GATE, int SCALE, int FIT>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k_head(const LaunchArgs P) {
+  using K = Kind<BITS>;
+  constexpr bool INT = K::is_int;
+  constexpr float QMAX = (float)K::qmax_i;
+  __shared__ Shared sh;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int row = 64 * w + l;
+  const int item = blockIdx.x;
+  const int b = item / P.n_list;
+  const int h = P.head_list[item - b * P.n_list];
+  const size_t bh = (size_t)b * P.H + h;
+  const int slot = P.slots[b];
+
+  if (slot < 0 || slot >= P.num_slots) {
+    if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
+    if (MODE == MODE_STEP && w == 0) {
+      P.o[bh * kDim + l] = 0.0f;     // wave 0 and 1 cover columns 0..127
+      P.o[bh * kDim + 64 + l] = 0.0f;
+    }
+    if (MODE == MODE_UNPACK) {
+      float *dst = P.S_out + bh * kDim * kDim;
+      for (int i = 0; i < 64; ++i) { dst[(64 * w + i) * kDim + l] = 0.0f; dst[(64 * w + i) * kDim + 64 + l] = 0.0f; }
+    }
+    return;
+  }
+  uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + P.heads[h].off;
+  uint4 *gran = reinterpret_cast<uint4 *>(blk);
+  float *rbuf = reinterpret_cast<float *>(blk + P.heads[h].code_bytes);
+  float *cbuf = rbuf + kDim;
+
+  float S[2][64];
+  float colc[2] = {1.0f, 1.0f};
+
+  // ---------------- load codes (both columns of this lane, this wave's rows)
+  uint32_t wd[2][K::NW];
+  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int g = 0; g < K::NG; ++g) {
+        const uint4 t = gran[(size_t)(w * K::NG + g) * kDim + (l + 64 * c)];
+        wd[c][4 * g + 0] = t.x; wd[c][4 * g + 1] = t.y; wd[c][4 * g + 2] = t.z; wd[c][4 * g + 3] = t.w;
+      }
+    }
+  }
+
+  // ---------------- per-row scalars of this lane's row, broadcast via LDS
+  float a_row = 1.0f;
+  if (MODE == MODE_STEP) {
+    a_row = (GATE == 0) ? P.gate[bh] : P.gate[bh * kDim + row];
+  }
+  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+    if (INT) {
+      const float r_row = rbuf[row];
+      sh.g[row] = a_row * rn_div(r_row, QMAX);
+      if (SCALE == 0) { colc[0] = cbuf[l]; colc[1] = cbuf[l + 64]; }
+    } else {
+      sh.g[row] = a_row;
+    }
+  }
+  float vcol[2] = {0.0f, 0.0f};
+  if (MODE == MODE_STEP) {
+    const float kr = P.k[bh * kDim + row];
+    sh.k[row] = kr;
+    sh.b[row] = P.beta[bh] * kr;
+    sh.q[row] = P.q[bh * kDim + row];
+    vcol[0] = P.v[bh * kDim + l];
+    vcol[1] = P.v[bh * kDim + 64 + l];
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---------------- restore (and gate)
+  if (MODE == MODE_STEP || MODE == MODE_UNPACK) restore_rows<BITS>(S, wd, colc, sh.g, 64 * w);
+
+  if (MODE == MODE_UNPACK) {
+    float *dst = P.S_out + bh * kDim * kDim;
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) {
+      dst[(64 * w + ii) * kDim + l] = S[0][ii];
+      dst[(64 * w + ii) * kDim + 64 + l] = S[1][ii];
+    }
+    return;
+  }
+
+  if (MODE == MODE_PACK) {
+    const float *src = P.S_in + bh * kDim * kDim;
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) {
+      S[0][ii] = src[(64 * w + ii) * kDim + l];
+      S[1][ii] = src[(64 * w + ii) * kDim + 64 + l];
+    }
+  }
+  if (MODE == MODE_RESET) {
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) { S[0][ii] = 0.0f; S[1][ii] = 0.0f; }
+  }
+
+  // ---------------- delta update (u chain: wave 0 rows 0..63, then wave 1)
+  float ocol[2] = {0.0f, 0.0f};
+  if (MODE == MODE_STEP) {
+    float u[2] = {0.0f, 0.0f};
+    if (w == 0) {
+      key_chain(S, u, sh.k, 0);
+      sh.x[l] = u[0];
+      sh.x[l + 64] = u[1];
+    }
+    __syncthreads();
+    if (w == 1) {
+      u[0] = sh.x[l];
+      u[1] = sh.x[l + 64];
+      key_chain(S, u, sh.k, 64);
+      sh.d[l] = vcol[0] - u[0];
+      sh.d[l + 64] = vcol[1] - u[1];
+    }
+    __syncthreads();
+    const float dl[2] = {sh.d[l], sh.d[l + 64]};
+#pragma unroll
+    for (int i4 = 0; i4 < 16; ++i4) {
+      const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
+      const float4 q4 = lds4(&sh.q[64 * w + 4 * i4]);
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+      const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 4 * i4 + e;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float s = __builtin_fmaf(bb[e], dl[c], S[c][ii]);
+          S[c][ii] = s;
+          ocol[c] = __builtin_fmaf(qq[e], s, ocol[c]);
+        }
+      }
+    }
+  }
+
+  // ---------------- requantise
+  uint32_t ow[2][K::NW];
+  if (INT) {
+    // row factor
+    float r_row, m_row = 0.0f;
+    if (SCALE == 0) {
+      m_row = row_reduce<false>(S, sh.red[w], l) * 0.0078125f;
+      const float nu = rn_div(m_row, P.omega[(size_t)h * kDim + row]);
+      r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
+    } else {
+      const float mx = row_reduce<true>(S, sh.red[w], l);
+      r_row = (mx < FLT_MIN) ? 1.0f : mx;
+    }
+    sh.ir[row] = rn_div(1.0f, r_row);
+    if (FIT) sh.m[row] = m_row;
+    rbuf[row] = r_row;
+    __builtin_amdgcn_wave_barrier();
+
+    // Y = S / r (in place) and the column maximum
+    float cm[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int i4 = 0; i4 < 16; ++i4) {
+      const float4 r4 = lds4(&sh.ir[64 * w + 4 * i4]);
+      const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float y = S[c][4 * i4 + e] * rr[e];
+          S[c][4 * i4 + e] = y;
+          cm[c] = fmaxf(cm[c], fabsf(y));
+        }
+      }
+    }
+    float c0[2] = {1.0f, 1.0f};
+    if (SCALE == 0) {
+      sh.cmax[w][l] = cm[0];
+      sh.cmax[w][l + 64] = cm[1];
+    }
+    if (MODE == MODE_STEP && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
+    __syncthreads();
+    if (SCALE == 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float mx = fmaxf(sh.cmax[0][l + 64 * c], sh.cmax[1][l + 64 * c]);
+        c0[c] = (mx < FLT_MIN) ? 1.0f : mx;
+      }
+    }
+    float wq[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) wq[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) * QMAX : QMAX;
+
+    // codes
+    float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
+    constexpr float INVQ = INT ? 1.0f / (QMAX > 0.0f ? QMAX : 1.0f) : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int i4 = 0; i4 < 16; ++i4) {
+        float mm[4] = {0, 0, 0, 0};
+        if (FIT) {
+          const float4 m4 = lds4(&sh.m[64 * w + 4 * i4]);
+          mm[0] = m4.x; mm[1] = m4.y; mm[2] = m4.z; mm[3] = m4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = 4 * i4 + e;
+          const float t = __builtin_fmaf(S[c][ii], wq[c], kMagic);
+          put_field<BITS>(ow[c], acc, __float_as_uint(t), ii);
+          if (FIT && w == 0) {
+            const float zeta = (t - kMagic) * INVQ;
+            const float pz = mm[e] * zeta;
+            nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
+            dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
+          }
+        }
+      }
+    }
+    // column factor
+    if (SCALE == 0) {
+      if (!FIT) {
+        if (w == 0) { cbuf[l] = c0[0]; cbuf[l + 64] = c0[1]; }
+      } else {
+        if (w == 0) {
+          sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
+          sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];
+        }
+        __syncthreads();
+        if (w == 1) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float nn = sh.d[l + 64 * c], dd = sh.y[l + 64 * c];
+#pragma unroll
+            for (int i4 = 0; i4 < 16; ++i4) {
+              const float4 m4 = lds4(&sh.m[64 + 4 * i4]);
+              const float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float t = __builtin_fmaf(S[c][4 * i4 + e], wq[c], kMagic);
+                const float zeta = (t - kMagic) * INVQ;
+                const float pz = mm[e] * zeta;
+                nn = __builtin_fmaf(pz, S[c][4 * i4 + e], nn);
+                dd = __builtin_fmaf(pz, zeta, dd);
+              }
+            }
+            cbuf[l + 64 * c] = (dd > 0.0f) ? rn_div(nn, dd) : c0[c];
+          }
+        }
+      }
+    }
+  } else {
+    // FP16 / FP32 rows: store the updated values themselves
+    if (MODE == MODE_STEP && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int ii = 0; ii < 64; ++ii) {
+        uint32_t f;
+        if (BITS == 16) f = (uint32_t)__half_as_ushort(__float2half_rn(S[c][ii]));
+        else f = __float_as_uint(S[c][ii]);
+        put_field<BITS>(ow[c], acc, f, ii);
+      }
+    }
+  }
+
+  // ---------------- store codes and the readout
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int g = 0; g < K::NG; ++g) {
+      uint4 t;
+      t.x = ow[c][4 * g + 0]; t.y = ow[c][4 * g + 1]; t.z = ow[c][4 * g + 2]; t.w = ow[c][4 * g + 3];
+      gran[(size_t)(w * K::NG + g) * kDim + (l + 64 * c)] = t;
+    }
+  }
+  if (MODE == MODE_STEP && w == 0) {
+    P.o[bh * kDim + l] = ocol[0] + sh.x[l];
+    P.o[bh * kDim + 64 + l] = ocol[1] + sh.x[l + 64];
+  }
+}
+
+// --------------------------------------------------------------------------
+// dispatch
+// --------------------------------------------------------------------------
+namespace {
+
+template <int BITS, int MODE>
+hipError_t launch_head_kind(const PoolConfig &cfg, const LaunchArgs &a, int n, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)n * a.n_list)), block(128);
+  if (grid.x == 0) return hipSuccess;
+  const bool dual = cfg.scale_mode == 0;
+  const bool fit = cfg.fit_iters > 0;
+  const bool diag = cfg.gate == 1;
+  if (!Kind<BITS>::is_int) {
+    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 0>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 0, 0>), grid, block, 0, st, a);
+  } else if (!dual) {
+    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 1, 0>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 1, 0>), grid, block, 0, st, a);
+  } else if (fit) {
+    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 1>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 0, 1>), grid, block, 0, st, a);
+  } else {
+    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 0>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 0, 0>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_heads(const PoolConfig &cfg, LaunchArgs a, int n, const int32_t *const *lists,
+                        const int32_t *counts, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  for (int kidx = 0; kidx < 6 && e == hipSuccess; ++kidx) {
+    if (counts[kidx] == 0) continue;
+    a.head_list = lists[kidx];
+    a.n_list = counts[kidx];
+    switch (kidx) {
+      case 0: e = launch_head_kind<2, MODE>(cfg, a, n, st); break;
+      case 1: e = launch_head_kind<4, MODE>(cfg, a, n, st); break;
+      case 2: e = launch_head_kind<6, MODE>(cfg, a, n, st); break;
+      case 3: e = launch_head_kind<8, MODE>(cfg, a, n, st); break;
+      case 4: e = launch_head_kind<16, MODE>(cfg, a, n, st); break;
+      default: e = launch_head_kind<32, MODE>(cfg, a, n, st); break;
+    }
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const int32_t *const *kind_lists,
+                      const int32_t *kind_counts, int mode, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (cfg.unit != 0) return hipErrorNotSupported;
+  switch (mode) {
+    case MODE_STEP: return launch_heads<MODE_STEP>(cfg, args, n, kind_lists, kind_counts, stream);
+    case MODE_PACK: return launch_heads<MODE_PACK>(cfg, args, n, kind_lists, kind_counts, stream);
+    case MODE_UNPACK: return launch_heads<MODE_UNPACK>(cfg, args, n, kind_lists, kind_counts, stream);
+    default: return launch_heads<MODE_RESET>(cfg, args, n, kind_lists, kind_counts, stream);
+  }
+}
+
+}  // namespace qdr

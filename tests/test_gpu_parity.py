@@ -1,0 +1,259 @@
+"""Device parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case feeds identical seeded inputs to both sides; the oracle never sees a
+byte produced by the device.  Bar: see tests/parity.py (packed bytes exact up
+to excused rounding ties, readout relative L2 <= 1e-4).
+"""
+import numpy as np
+import pytest
+
+from quantized_delta_rule_decode_amd import qdr, synth
+
+import parity
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "device tests need a HIP GPU"
+    qdr.load()
+    return torch
+
+
+def t_(torch, x, dtype=None):
+    a = np.ascontiguousarray(x)
+    t = torch.from_numpy(a).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def edge_states(seed, n, H):
+    """Random outlier states plus degenerate heads: zero head, zero rows,
+    zero columns, tiny magnitudes, large dynamic range."""
+    S = synth.random_state(seed, n, H)
+    if H >= 4:
+        S[0, 0] = 0.0
+        S[0, 1, 5:9] = 0.0
+        S[0, 2, :, 17] = 0.0
+        S[0, 2, :, 100] = 0.0
+        S[-1, 3] *= np.float32(1e-30)
+    if n > 1 and H >= 2:
+        S[1, 1, 3] *= np.float32(1e6)
+    return S
+
+
+HEAD_KIND_SETS = {
+    "int_all": [2, 4, 6, 8, 6, 8],
+    "with_pivots": [16, 8, 6, 4, 16, 2],
+    "fp32": [32, 32],
+}
+
+
+def make_pair(orc, num_slots, kinds, omega, unit=0, gate=0, scale=0, fit=0):
+    H = len(kinds) if unit == 0 else len(kinds) // D
+    dev = qdr.Pool(num_slots, H, kinds, omega, unit=unit, gate=gate, scale_mode=scale, fit_iters=fit)
+    ref = orc.Pool(num_slots, H, kinds, omega, unit=unit, gate=gate, scale_mode=scale,
+                   fit_iters=fit).alloc()
+    assert dev.slot_stride == ref.slot_stride
+    assert np.array_equal(dev.head_off, ref.head_off.astype(np.uint64))
+    return dev, ref
+
+
+@pytest.mark.parametrize("name", sorted(HEAD_KIND_SETS))
+@pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
+def test_pack_parity(torch_dev, orc, name, scale, fit):
+    torch = torch_dev
+    kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
+    H = kinds.size
+    omega = np.random.default_rng(1).lognormal(0, 1, (H, D)).astype(np.float32)
+    dev, ref = make_pair(orc, 5, kinds, omega, scale=scale, fit=fit)
+    slots = np.array([3, 0, 4], np.int32)
+    S = edge_states(7, 3, H)
+    dev.qdr_pack(t_(torch, slots), t_(torch, S))
+    ref.pack(slots, S)
+    torch.cuda.synchronize()
+    rep = parity.StepReport()
+    parity.compare_pool(orc, ref, dev, slots, lambda b, h: S[b, h], rep, resync=False)
+    parity.assert_step_ok(rep, f"pack {name} scale={scale} fit={fit}")
+    assert rep.blocks_mismatched == 0
+
+
+@pytest.mark.parametrize("name", sorted(HEAD_KIND_SETS))
+@pytest.mark.parametrize("scale", [0, 1])
+def test_unpack_parity(torch_dev, orc, name, scale):
+    torch = torch_dev
+    kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
+    H = kinds.size
+    omega = np.random.default_rng(2).lognormal(0, 1, (H, D)).astype(np.float32)
+    dev, ref = make_pair(orc, 3, kinds, omega, scale=scale)
+    S = edge_states(8, 3, H)
+    ref.pack(np.arange(3, dtype=np.int32), S)
+    for s in range(3):
+        dev.qdr_write_raw(s, ref.mem[s * ref.slot_stride:(s + 1) * ref.slot_stride])
+    slots = np.array([2, -1, 0], np.int32)
+    out = torch.full((3, H, D, D), 7.0, dtype=torch.float32, device="cuda")
+    dev.qdr_unpack(t_(torch, slots), out)
+    X_ref = ref.unpack(slots)
+    X_dev = out.cpu().numpy()
+    assert np.array_equal(X_dev.view(np.uint32), X_ref.view(np.uint32))
+
+
+def test_reset_encodes_zero(torch_dev, orc):
+    torch = torch_dev
+    kinds = np.array([2, 4, 6, 8, 16, 32], np.uint8)
+    omega = np.ones((6, D), np.float32)
+    for scale in (0, 1):
+        dev, ref = make_pair(orc, 4, kinds, omega, scale=scale)
+        slots = np.array([1, 3], np.int32)
+        dev.qdr_slot_reset(t_(torch, slots))
+        ref.pack(slots, np.zeros((2, 6, D, D), np.float32))
+        for s in range(4):
+            assert np.array_equal(dev.qdr_read_raw(s), ref.mem[s * ref.slot_stride:(s + 1) * ref.slot_stride])
+
+
+def random_inputs(seed, B, H, gate_diag):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((B, H, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True) * np.sqrt(D)
+    k = g.standard_normal((B, H, D))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = g.standard_normal((B, H, D)) * g.lognormal(0, 1, (1, H, D))
+    beta = g.uniform(0, 1, (B, H))
+    gate = g.uniform(0.5, 1.0, (B, H, D) if gate_diag else (B, H))
+    return tuple(np.ascontiguousarray(x, np.float32) for x in (q, k, v, beta, gate))
+
+
+def run_step_pair(torch, orc, dev, ref, slots, inputs, threads=8):
+    prev = ref.mem.copy()
+    dev_in = [t_(torch, x) for x in inputs]
+    o = torch.full((slots.size, dev.num_heads, D), 3.0, dtype=torch.float32, device="cuda")
+    dev.qdr_decode_step(t_(torch, slots), *dev_in, o)
+    o_ref, bad = ref.step(slots, *inputs, threads=threads)
+    o_dev = o.cpu().numpy()
+    rep = parity.StepReport()
+    parity.compare_o(o_dev, o_ref, rep)
+    parity.compare_pool(orc, ref, dev, slots, parity.step_state_fn(orc, ref, prev, slots, inputs), rep)
+    return rep, o_dev, o_ref, bad
+
+
+@pytest.mark.parametrize("name", sorted(HEAD_KIND_SETS))
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
+def test_single_step_parity(torch_dev, orc, name, gate, scale, fit):
+    torch = torch_dev
+    kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
+    H = kinds.size
+    omega = np.random.default_rng(3).lognormal(0, 1, (H, D)).astype(np.float32)
+    dev, ref = make_pair(orc, 6, kinds, omega, gate=gate, scale=scale, fit=fit)
+    S = edge_states(11, 6, H)
+    all_slots = np.arange(6, dtype=np.int32)
+    dev.qdr_pack(t_(torch, all_slots), t_(torch, S))
+    ref.pack(all_slots, S)
+    slots = np.array([4, -1, 0, 5, 2], np.int32)     # padding row and a ragged subset
+    inputs = random_inputs(12, slots.size, H, gate == 1)
+    rep, o_dev, o_ref, bad = run_step_pair(torch, orc, dev, ref, slots, inputs)
+    parity.assert_step_ok(rep, f"step {name} gate={gate} scale={scale} fit={fit}")
+    assert bad == 0
+    assert np.all(o_dev[1] == 0)
+    # untouched slots keep their bytes
+    for s in (1, 3):
+        assert np.array_equal(dev.qdr_read_raw(s), ref.mem[s * ref.slot_stride:(s + 1) * ref.slot_stride])
+    assert dev.qdr_poll_device_error() == 0
+
+
+def test_bad_slots_flag_and_zero_output(torch_dev, orc):
+    torch = torch_dev
+    kinds = np.array([6, 8], np.uint8)
+    omega = np.ones((2, D), np.float32)
+    dev, ref = make_pair(orc, 3, kinds, omega)
+    dev.qdr_slot_reset(t_(torch, np.arange(3, dtype=np.int32)))
+    before = [dev.qdr_read_raw(s) for s in range(3)]
+    slots = np.array([7, -1, -5], np.int32)
+    inputs = random_inputs(5, 3, 2, False)
+    o = torch.full((3, 2, D), 9.0, dtype=torch.float32, device="cuda")
+    dev.qdr_decode_step(t_(torch, slots), *[t_(torch, x) for x in inputs], o)
+    assert torch.all(o == 0).item()
+    assert dev.qdr_poll_device_error() == qdr.DEVERR_SLOT
+    assert dev.qdr_poll_device_error() == 0
+    for s in range(3):
+        assert np.array_equal(dev.qdr_read_raw(s), before[s])
+
+
+def test_empty_batch_is_noop(torch_dev, orc):
+    torch = torch_dev
+    dev, _ = make_pair(orc, 2, np.array([6], np.uint8), np.ones((1, D), np.float32))
+    z = torch.empty(0, dtype=torch.float32, device="cuda")
+    dev.qdr_decode_step(torch.empty(0, dtype=torch.int32, device="cuda"), z, z, z, z, z, z)
+
+
+def test_deterministic(torch_dev, orc):
+    torch = torch_dev
+    kinds = np.array([2, 4, 6, 8, 16], np.uint8)
+    omega = np.random.default_rng(4).lognormal(0, 1, (5, D)).astype(np.float32)
+    outs = []
+    for _ in range(2):
+        dev, _ = make_pair(orc, 2, kinds, omega)
+        dev.qdr_pack(t_(torch, np.arange(2, dtype=np.int32)), t_(torch, edge_states(3, 2, 5)))
+        inputs = random_inputs(6, 2, 5, False)
+        o = torch.empty((2, 5, D), dtype=torch.float32, device="cuda")
+        dev.qdr_decode_step(t_(torch, np.arange(2, dtype=np.int32)), *[t_(torch, x) for x in inputs], o)
+        outs.append((dev.qdr_read_raw(0), dev.qdr_read_raw(1), o.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------- configs
+def trajectory(torch, orc, cid, steps, threads=16):
+    from quantized_delta_rule_decode_amd import workload
+    cfg = synth.CONFIGS[cid]
+    t = synth.static_tables(cfg)
+    dev = workload.make_pool(cfg, t)
+    ref = orc.Pool(cfg.num_slots, cfg.H, t["kinds"], t["omega"], unit=cfg.unit, gate=cfg.gate,
+                   scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters).alloc()
+    slots = t["slots"]
+    slots_t = t_(torch, slots)
+    if cfg.warmup:
+        # FP32 warm-up on both sides, then pack (config 1)
+        f32 = workload.warm_start(cfg, t, dev, slots_t, cfg.warmup)
+        S32_dev = torch.empty((cfg.B, cfg.H, D, D), dtype=torch.float32, device="cuda")
+        f32.qdr_unpack(t_(torch, np.arange(cfg.B, dtype=np.int32)), S32_dev)
+        ref32 = orc.Pool(cfg.B, cfg.H, np.full(cfg.H, 32, np.uint8), np.ones((cfg.H, D), np.float32),
+                         gate=cfg.gate).alloc()
+        ref32.pack(np.arange(cfg.B, dtype=np.int32), np.zeros((cfg.B, cfg.H, D, D), np.float32))
+        for s in range(cfg.warmup):
+            ref32.step(np.arange(cfg.B, dtype=np.int32), *synth.step_inputs(cfg, t, s, warmup=True),
+                       threads=threads)
+        S32 = ref32.unpack(np.arange(cfg.B, dtype=np.int32))
+        assert np.array_equal(S32_dev.cpu().numpy().view(np.uint32), S32.view(np.uint32)), \
+            "FP32 warm-up trajectory differs"
+        ref.pack(slots, S32)
+    else:
+        dev.qdr_slot_reset(slots_t)
+        ref.pack(slots, np.zeros((cfg.B, cfg.H, D, D), np.float32))
+    torch.cuda.synchronize()
+    for s in slots:
+        s = int(s)
+        assert np.array_equal(dev.qdr_read_raw(s), ref.mem[s * ref.slot_stride:(s + 1) * ref.slot_stride]), \
+            f"initial pool differs in slot {s}"
+    worst = 0.0
+    excused = 0
+    for s in range(steps):
+        inputs = synth.step_inputs(cfg, t, s)
+        rep, _, _, bad = run_step_pair(torch, orc, dev, ref, slots, inputs, threads=threads)
+        parity.assert_step_ok(rep, f"config {cid} step {s}")
+        assert bad == 0
+        worst = max(worst, rep.o_rel_l2)
+        excused += rep.codes_excused
+    return worst, excused
+
+
+def test_config1_trajectory(torch_dev, orc):
+    worst, excused = trajectory(torch_dev, orc, 1, synth.CONFIGS[1].steps)
+    assert worst <= 1e-4
+
+
+def test_config2_trajectory(torch_dev, orc):
+    worst, excused = trajectory(torch_dev, orc, 2, 48)
+    assert worst <= 1e-4

@@ -51,7 +51,26 @@ struct Kind {
 };
 
 __device__ __forceinline__ float rn_div(float a, float b) { return __fdiv_rn(a, b); }
-__device__ __forceinline__ float rn_sqrt(float a) { return __fsqrt_rn(a); }
+
+// Correctly rounded square root of a finite x >= 0.  v_sqrt_f32 is accurate
+// to one ulp; the neighbours s-ulp and s+ulp are then tested exactly: for
+// adjacent floats a < b, a*b equals the squared midpoint minus (b-a)^2/4, and
+// no float lies strictly between the two, so the sign of the single-rounded
+// residual x - a*b (an fma) tells on which side of the midpoint sqrt(x) lies.
+// Inputs below 2^-100 are scaled by 2^64 first so the residuals stay
+// representable.  (A square root is never exactly halfway between floats.)
+__device__ __forceinline__ float rn_sqrt(float x) {
+  const bool tiny = x < 0x1p-100f;
+  const float xs = tiny ? x * 0x1p64f : x;
+  float s = __builtin_amdgcn_sqrtf(xs);
+  const float s_dn = __uint_as_float(__float_as_uint(s) - 1u);
+  const float s_up = __uint_as_float(__float_as_uint(s) + 1u);
+  const float r_dn = __builtin_fmaf(-s_dn, s, xs);
+  const float r_up = __builtin_fmaf(-s_up, s, xs);
+  s = (r_dn <= 0.0f) ? s_dn : s;
+  s = (r_up > 0.0f) ? s_up : s;
+  return tiny ? s * 0x1p-32f : s;
+}
 
 // b-bit field number `ii` of a column-half stream held in w[] (two's
 // complement for integer kinds, raw bits otherwise).

@@ -63,6 +63,10 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with quantized_delta_rule_decode_amd/build.py")
+    # torch's HIP runtime must be the process's HIP runtime: importing torch
+    # first makes libqdr.so bind to the already loaded libamdhip64.so.7
+    # instead of loading a second runtime instance.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {

@@ -42,6 +42,12 @@ namespace {
 // exact product Y*w and yields the code's bit pattern.
 constexpr float kMagic = 12582912.0f;
 
+// Scheduling fences between groups of rows keep the unrolled loops from
+// hoisting whole phases (which would hold every unpacked code next to the
+// tile); LDS and global reads may still move up, so the next group's
+// row scalars are fetched while the current group computes.
+#define QDR_FENCE() __builtin_amdgcn_sched_barrier(0x0120)
+
 template <int BITS>
 struct Kind {
   static constexpr bool is_int = BITS <= 8;
@@ -51,6 +57,15 @@ struct Kind {
 };
 
 __device__ __forceinline__ float rn_div(float a, float b) { return __fdiv_rn(a, b); }
+
+// Pins x to an fp32 register: an empty asm statement with a read-write VGPR
+// operand.  Without it the compiler folds fp16_round(fma(a, b, c)) into one
+// mixed-precision fma that rounds the exact result to fp16 once, which
+// differs from rounding to fp32 first (the state is fp32) at fp16 ties.
+__device__ __forceinline__ float pin_f32(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Correctly rounded square root of a finite x >= 0.  v_sqrt_f32 is accurate
 // to one ulp; the neighbours s-ulp and s+ulp are then tested exactly: for
@@ -112,6 +127,44 @@ __device__ __forceinline__ void put_field(uint32_t *out, uint32_t &acc, uint32_t
   }
 }
 
+// Block accesses go through a buffer resource (base and size of the block in
+// SGPRs): a code granule is (scalar offset of granule row g of this wave) +
+// (one 32-bit lane offset), so no per-granule 64-bit vector address stays
+// live between the loads and the stores, and accesses past the block end are
+// dropped by the hardware range check.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) dword access on CDNA
+
+__device__ __forceinline__ uint4 load_granule(rsrc_t rs, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void store_granule(rsrc_t rs, uint4 t, uint32_t voff, uint32_t soff) {
+  __attribute__((ext_vector_type(4))) unsigned int v = {t.x, t.y, t.z, t.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, 0);
+}
+
+__device__ __forceinline__ float load_f32(rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+}
+
+__device__ __forceinline__ void store_f32(rsrc_t rs, float x, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(x), rs, voff, soff, 0);
+}
+
+// Store one column half (this wave's 64 rows of column j) as 16-byte granules.
+// soff0: byte offset of this wave's first granule row; voff = j*16.
+template <int BITS>
+__device__ __forceinline__ void store_column(rsrc_t rs, const uint32_t *ow, uint32_t voff, uint32_t soff0) {
+#pragma unroll
+  for (int g = 0; g < Kind<BITS>::NG; ++g) {
+    uint4 t;
+    t.x = ow[4 * g + 0]; t.y = ow[4 * g + 1]; t.z = ow[4 * g + 2]; t.w = ow[4 * g + 3];
+    store_granule(rs, t, voff, soff0 + (uint32_t)g * (kDim * 16));
+  }
+}
+
 __device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
 // Row reduction of |S| over the 128 columns of each of this wave's 64 rows.
@@ -122,33 +175,29 @@ __device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cas
 // 64w + lane.  red: this wave's [64][20] LDS scratch.
 template <bool MAX>
 __device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red)[20], int lane) {
-  // level j/j+64 is lane-local; it is formed pair by pair so that only the
-  // 32 level-two partials are live next to the tile
-  float q1[32];
-#pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const float p0 = MAX ? fmaxf(fabsf(S[0][2 * t]), fabsf(S[1][2 * t]))
-                         : fabsf(S[0][2 * t]) + fabsf(S[1][2 * t]);
-    const float p1 = MAX ? fmaxf(fabsf(S[0][2 * t + 1]), fabsf(S[1][2 * t + 1]))
-                         : fabsf(S[0][2 * t + 1]) + fabsf(S[1][2 * t + 1]);
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-    const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
-    q1[t] = MAX ? fmaxf(x, y) : x + y;
-  }
-  float q2[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(q1[2 * s]), __float_as_uint(q1[2 * s + 1]),
-                                               false, false);
-    const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
-    q2[s] = MAX ? fmaxf(x, y) : x + y;
-  }
-  // lane group G = lane/16 now holds rows 4s + {0,2,1,3}[G]; n = lane%16 is
-  // the column residue of the partial.
+  // rows are taken four at a time so that only a handful of partials are
+  // live next to the tile: rows 4s..4s+3 -> two permlane32 partials -> one
+  // permlane16 partial holding row 4s + {0,2,1,3}[lane/16] for column
+  // residue lane%16, written to LDS.
   const int G = lane >> 4, n = lane & 15;
   const int rsub = (G == 0) ? 0 : (G == 1) ? 2 : (G == 2) ? 1 : 3;
 #pragma unroll
-  for (int s = 0; s < 16; ++s) red[4 * s + rsub][n] = q2[s];
+  for (int s = 0; s < 16; ++s) {
+    float h1[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 4 * s + 2 * t, r1 = r0 + 1;
+      const float p0 = MAX ? fmaxf(fabsf(S[0][r0]), fabsf(S[1][r0])) : fabsf(S[0][r0]) + fabsf(S[1][r0]);
+      const float p1 = MAX ? fmaxf(fabsf(S[0][r1]), fabsf(S[1][r1])) : fabsf(S[0][r1]) + fabsf(S[1][r1]);
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+      const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
+      h1[t] = MAX ? fmaxf(x, y) : x + y;
+    }
+    auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h1[0]), __float_as_uint(h1[1]), false, false);
+    const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
+    red[4 * s + rsub][n] = MAX ? fmaxf(x, y) : x + y;
+    if (s & 1) QDR_FENCE();
+  }
   __builtin_amdgcn_wave_barrier();
   float x[16];
 #pragma unroll
@@ -165,14 +214,21 @@ __device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red
   return x[0];
 }
 
+
 // Restore this wave's 64 rows of both lane columns into S (gate included).
-template <int BITS>
-__device__ __forceinline__ void restore_rows(float (&S)[2][64], const uint32_t (&wd)[2][Kind<BITS>::NW],
-                                             const float (&colc)[2], const float *gsh, int row0) {
+// CHAIN also runs acc_c = fma(x_i, S'_ic, acc_c) over those rows in order.
+template <int BITS, bool CHAIN>
+__device__ __forceinline__ void restore_rows(float (&S)[2][64], float (&acc)[2],
+                                             const uint32_t (&wd)[2][Kind<BITS>::NW],
+                                             const float (&colc)[2], const float *gsh,
+                                             const float *xsh, int row0) {
 #pragma unroll
   for (int i4 = 0; i4 < 16; ++i4) {
     const float4 g4 = lds4(&gsh[row0 + 4 * i4]);
+    float4 x4 = {0, 0, 0, 0};
+    if (CHAIN) x4 = lds4(&xsh[row0 + 4 * i4]);
     const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+    const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ii = 4 * i4 + e;
@@ -188,26 +244,32 @@ __device__ __forceinline__ void restore_rows(float (&S)[2][64], const uint32_t (
           sp = gg[e] * __uint_as_float(field_bits<32>(wd[c], ii));
         }
         S[c][ii] = sp;
+        if (CHAIN) acc[c] = __builtin_fmaf(xx[e], sp, acc[c]);
       }
     }
-    // keep the scheduler from hoisting every extraction ahead of use, which
-    // would hold all 128 unpacked codes next to the tile
-    __builtin_amdgcn_sched_barrier(0);
+    QDR_FENCE();
   }
 }
 
-// Continue the key-projection chains u_c over this wave's 64 rows, in order.
-__device__ __forceinline__ void key_chain(const float (&S)[2][64], float (&u)[2], const float *ksh, int row0) {
+// acc_c = fma(x_i, S_ic, acc_c) over this wave's 64 rows, in order.
+__device__ __forceinline__ void chain_rows(const float (&S)[2][64], float (&acc)[2], const float *xsh, int row0) {
 #pragma unroll
   for (int i4 = 0; i4 < 16; ++i4) {
-    const float4 k4 = lds4(&ksh[row0 + 4 * i4]);
-    const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+    const float4 x4 = lds4(&xsh[row0 + 4 * i4]);
+    const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      u[0] = __builtin_fmaf(kk[e], S[0][4 * i4 + e], u[0]);
-      u[1] = __builtin_fmaf(kk[e], S[1][4 * i4 + e], u[1]);
+      acc[0] = __builtin_fmaf(xx[e], S[0][4 * i4 + e], acc[0]);
+      acc[1] = __builtin_fmaf(xx[e], S[1][4 * i4 + e], acc[1]);
     }
+    QDR_FENCE();
   }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
 }
 
 struct Shared {
@@ -221,6 +283,7 @@ struct Shared {
   float d[kDim];     // delta, then refit numerator hand-off
   float y[kDim];     // refit denominator hand-off
   float cmax[2][kDim];
+  float qb[2];       // each wave's part of sum_i q_i b_i
   float red[2][64][20];
 };
 
@@ -232,8 +295,19 @@ struct Shared {
 // MODE_PACK: requantise S_in.  MODE_UNPACK: restore into S_out.
 // MODE_RESET: requantise S = 0.
 // --------------------------------------------------------------------------
+// Waves per SIMD the register allocation targets: three for the dual-axis
+// integer kernels (their 128-register tile plus working set fits in 168
+// VGPRs), two where it does not (float kinds, the refit variant, the
+// row-absmax baseline).
+template <int BITS, int MODE, int SCALE, int FIT>
+struct Occupancy {
+  static constexpr int waves = (BITS <= 8 && FIT == 0 && SCALE == 0) ? 3 : 2;
+};
+
 template <int BITS, int MODE, int GATE, int SCALE, int FIT>
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k_head(const LaunchArgs P) {
+__global__ void __launch_bounds__(128)
+__attribute__((amdgpu_waves_per_eu(Occupancy<BITS, MODE, SCALE, FIT>::waves)))
+k_head(const LaunchArgs P) {
   using K = Kind<BITS>;
   constexpr bool INT = K::is_int;
   constexpr float QMAX = (float)K::qmax_i;
@@ -262,9 +336,12 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
     return;
   }
   uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + P.heads[h].off;
-  uint4 *gran = reinterpret_cast<uint4 *>(blk);
-  float *rbuf = reinterpret_cast<float *>(blk + P.heads[h].code_bytes);
-  float *cbuf = rbuf + kDim;
+  const uint32_t code_bytes = P.heads[h].code_bytes;
+  const uint32_t blk_bytes = code_bytes + (INT ? (SCALE == 0 ? 2u : 1u) * kDim * 4u : 0u);
+  const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(blk, 0, (int)blk_bytes, kRsrcWord3);
+  const uint32_t half_off = (uint32_t)w * K::NG * (kDim * 16);   // this wave's first granule row
+  const uint32_t r_off = code_bytes;                              // r[128]
+  const uint32_t c_off = code_bytes + kDim * 4;                   // c[128]
 
   float S[2][64];
   float colc[2] = {1.0f, 1.0f};
@@ -276,7 +353,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int g = 0; g < K::NG; ++g) {
-        const uint4 t = gran[(size_t)(w * K::NG + g) * kDim + (l + 64 * c)];
+        const uint4 t = load_granule(rs, (uint32_t)(l + 64 * c) * 16u, half_off + (uint32_t)g * (kDim * 16));
         wd[c][4 * g + 0] = t.x; wd[c][4 * g + 1] = t.y; wd[c][4 * g + 2] = t.z; wd[c][4 * g + 3] = t.w;
       }
     }
@@ -285,30 +362,42 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
   // ---------------- per-row scalars of this lane's row, broadcast via LDS
   float a_row = 1.0f;
   if (MODE == MODE_STEP) {
-    a_row = (GATE == 0) ? P.gate[bh] : P.gate[bh * kDim + row];
+    a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
   }
   if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
     if (INT) {
-      const float r_row = rbuf[row];
+      const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
       sh.g[row] = a_row * rn_div(r_row, QMAX);
-      if (SCALE == 0) { colc[0] = cbuf[l]; colc[1] = cbuf[l + 64]; }
+      if (SCALE == 0) {
+        colc[0] = load_f32(rs, (uint32_t)l * 4u, c_off);
+        colc[1] = load_f32(rs, (uint32_t)l * 4u + 256u, c_off);
+      }
     } else {
       sh.g[row] = a_row;
     }
   }
   float vcol[2] = {0.0f, 0.0f};
   if (MODE == MODE_STEP) {
-    const float kr = P.k[bh * kDim + row];
+    const float kr = (P.k + bh * kDim)[row];
     sh.k[row] = kr;
     sh.b[row] = P.beta[bh] * kr;
-    sh.q[row] = P.q[bh * kDim + row];
-    vcol[0] = P.v[bh * kDim + l];
-    vcol[1] = P.v[bh * kDim + 64 + l];
+    sh.q[row] = (P.q + bh * kDim)[row];
+    const float *vrow = P.v + bh * kDim;
+    vcol[0] = vrow[l];
+    vcol[1] = vrow[l + 64];
   }
   __builtin_amdgcn_wave_barrier();
 
-  // ---------------- restore (and gate)
-  if (MODE == MODE_STEP || MODE == MODE_UNPACK) restore_rows<BITS>(S, wd, colc, sh.g, 64 * w);
+  // ---------------- restore (and gate).  In a step the two waves balance the
+  // sequential key projection u = S'^T k (rows 0..63 by wave 0, then rows
+  // 64..127 by wave 1) against the readout part S'^T q of their own rows:
+  // wave 0 runs its half of u inside the restore and its q part after the
+  // hand-off, wave 1 the other way round.
+  float acc1[2] = {0.0f, 0.0f};
+  if (MODE == MODE_STEP)
+    restore_rows<BITS, true>(S, acc1, wd, colc, sh.g, (w == 0) ? sh.k : sh.q, 64 * w);
+  else if (MODE == MODE_UNPACK)
+    restore_rows<BITS, false>(S, acc1, wd, colc, sh.g, sh.g, 64 * w);
 
   if (MODE == MODE_UNPACK) {
     float *dst = P.S_out + bh * kDim * kDim;
@@ -333,52 +422,51 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
     for (int ii = 0; ii < 64; ++ii) { S[0][ii] = 0.0f; S[1][ii] = 0.0f; }
   }
 
-  // ---------------- delta update (u chain: wave 0 rows 0..63, then wave 1)
-  float ocol[2] = {0.0f, 0.0f};
+  // ---------------- delta update
+  float oq[2] = {0.0f, 0.0f};
+  float dl[2] = {0.0f, 0.0f};
   if (MODE == MODE_STEP) {
-    float u[2] = {0.0f, 0.0f};
-    if (w == 0) {
-      key_chain(S, u, sh.k, 0);
-      sh.x[l] = u[0];
-      sh.x[l + 64] = u[1];
-    }
+    if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
+    const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
+    if (l == 0) sh.qb[w] = qb_part;
     __syncthreads();
+    float acc2[2] = {0.0f, 0.0f};
+    if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
+    chain_rows(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
     if (w == 1) {
-      u[0] = sh.x[l];
-      u[1] = sh.x[l + 64];
-      key_chain(S, u, sh.k, 64);
-      sh.d[l] = vcol[0] - u[0];
-      sh.d[l + 64] = vcol[1] - u[1];
+      sh.d[l] = vcol[0] - acc2[0];
+      sh.d[l + 64] = vcol[1] - acc2[1];
+      oq[0] = acc1[0]; oq[1] = acc1[1];
+    } else {
+      oq[0] = acc2[0]; oq[1] = acc2[1];
     }
     __syncthreads();
-    const float dl[2] = {sh.d[l], sh.d[l + 64]};
+    dl[0] = sh.d[l];
+    dl[1] = sh.d[l + 64];
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
-      const float4 q4 = lds4(&sh.q[64 * w + 4 * i4]);
       const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-      const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 4 * i4 + e;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float s = __builtin_fmaf(bb[e], dl[c], S[c][ii]);
-          S[c][ii] = s;
-          ocol[c] = __builtin_fmaf(qq[e], s, ocol[c]);
-        }
+        S[0][ii] = __builtin_fmaf(bb[e], dl[0], S[0][ii]);
+        S[1][ii] = __builtin_fmaf(bb[e], dl[1], S[1][ii]);
       }
+      QDR_FENCE();
     }
   }
+  // readout (tolerance-checked, any summation order):
+  //   o = S_t^T q = S'^T q + (q . b) delta
+  float ocol[2] = {oq[0], oq[1]};
 
   // ---------------- requantise
-  uint32_t ow[2][K::NW];
   if (INT) {
     // row factor
     float r_row, m_row = 0.0f;
     if (SCALE == 0) {
       m_row = row_reduce<false>(S, sh.red[w], l) * 0.0078125f;
-      const float nu = rn_div(m_row, P.omega[(size_t)h * kDim + row]);
+      const float nu = rn_div(m_row, (P.omega + (size_t)h * kDim)[row]);
       r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
     } else {
       const float mx = row_reduce<true>(S, sh.red[w], l);
@@ -386,7 +474,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
     }
     sh.ir[row] = rn_div(1.0f, r_row);
     if (FIT) sh.m[row] = m_row;
-    rbuf[row] = r_row;
+    store_f32(rs, r_row, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
     __builtin_amdgcn_wave_barrier();
 
     // Y = S / r (in place) and the column maximum
@@ -404,6 +492,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
           cm[c] = fmaxf(cm[c], fabsf(y));
         }
       }
+      QDR_FENCE();
     }
     float c0[2] = {1.0f, 1.0f};
     if (SCALE == 0) {
@@ -423,11 +512,12 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
 #pragma unroll
     for (int c = 0; c < 2; ++c) wq[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) * QMAX : QMAX;
 
-    // codes
+    // codes: pack and store one column at a time
     float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
     constexpr float INVQ = INT ? 1.0f / (QMAX > 0.0f ? QMAX : 1.0f) : 0.0f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      uint32_t ow[K::NW];
       uint32_t acc = 0;
 #pragma unroll
       for (int i4 = 0; i4 < 16; ++i4) {
@@ -440,20 +530,25 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
         for (int e = 0; e < 4; ++e) {
           const int ii = 4 * i4 + e;
           const float t = __builtin_fmaf(S[c][ii], wq[c], kMagic);
-          put_field<BITS>(ow[c], acc, __float_as_uint(t), ii);
-          if (FIT && w == 0) {
+          put_field<BITS>(ow, acc, __float_as_uint(t), ii);
+          if (FIT) {
             const float zeta = (t - kMagic) * INVQ;
             const float pz = mm[e] * zeta;
             nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
             dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
           }
         }
+        QDR_FENCE();
       }
+      store_column<BITS>(rs, ow, (uint32_t)(l + 64 * c) * 16u, half_off);
     }
     // column factor
     if (SCALE == 0) {
       if (!FIT) {
-        if (w == 0) { cbuf[l] = c0[0]; cbuf[l + 64] = c0[1]; }
+        if (w == 0) {
+          store_f32(rs, c0[0], (uint32_t)l * 4u, c_off);
+          store_f32(rs, c0[1], (uint32_t)l * 4u + 256u, c_off);
+        }
       } else {
         if (w == 0) {
           sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
@@ -477,7 +572,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
                 dd = __builtin_fmaf(pz, zeta, dd);
               }
             }
-            cbuf[l + 64 * c] = (dd > 0.0f) ? rn_div(nn, dd) : c0[c];
+            store_f32(rs, (dd > 0.0f) ? rn_div(nn, dd) : c0[c], (uint32_t)l * 4u + 256u * c, c_off);
           }
         }
       }
@@ -488,30 +583,25 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) k
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      uint32_t ow[K::NW];
       uint32_t acc = 0;
 #pragma unroll
       for (int ii = 0; ii < 64; ++ii) {
         uint32_t f;
-        if (BITS == 16) f = (uint32_t)__half_as_ushort(__float2half_rn(S[c][ii]));
+        if (BITS == 16) f = (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])));
         else f = __float_as_uint(S[c][ii]);
-        put_field<BITS>(ow[c], acc, f, ii);
+        put_field<BITS>(ow, acc, f, ii);
       }
+      store_column<BITS>(rs, ow, (uint32_t)(l + 64 * c) * 16u, half_off);
     }
   }
 
-  // ---------------- store codes and the readout
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-#pragma unroll
-    for (int g = 0; g < K::NG; ++g) {
-      uint4 t;
-      t.x = ow[c][4 * g + 0]; t.y = ow[c][4 * g + 1]; t.z = ow[c][4 * g + 2]; t.w = ow[c][4 * g + 3];
-      gran[(size_t)(w * K::NG + g) * kDim + (l + 64 * c)] = t;
-    }
-  }
+  // ---------------- the readout
   if (MODE == MODE_STEP && w == 0) {
-    P.o[bh * kDim + l] = ocol[0] + sh.x[l];
-    P.o[bh * kDim + 64 + l] = ocol[1] + sh.x[l + 64];
+    const float qb_all = sh.qb[0] + sh.qb[1];
+    float *orow = P.o + bh * kDim;
+    orow[l] = (ocol[0] + sh.x[l]) + qb_all * dl[0];
+    orow[l + 64] = (ocol[1] + sh.x[l + 64]) + qb_all * dl[1];
   }
 }
 

@@ -292,8 +292,9 @@ void or_head_step(int d, const uint8_t *kinds, uint32_t *e, float *r,
 /*    binary32); stream bit p is bit p%8 of stream byte p/8;                 */
 /*  - integer codes are stored as b-bit two's complement;                    */
 /*  - the stream is cut into granules of G bytes (G = 16 for whole-head      */
-/*    units, 4 for row units), zero-padded to whole granules; granule g of   */
-/*    column j sits at byte (g*128 + j)*G of the block;                      */
+/*    units, 4 for row units); rows 0..63 fill the first granules and rows   */
+/*    64..127 start on a fresh granule, each half zero-padded to whole       */
+/*    granules; granule g of column j sits at byte (g*128 + j)*G;            */
 /*  - then, if any row is an integer row: r[128] fp32, and in dual-axis mode */
 /*    c[128] fp32;                                                           */
 /*  - the block is zero-padded to a multiple of 256 bytes.                   */
@@ -306,11 +307,28 @@ static int any_int_row(const uint8_t *kinds) {
   return 0;
 }
 
-size_t or_code_bytes(const uint8_t *kinds, int unit) {
+/* granules of one half (rows lo..lo+63) of a column stream */
+static size_t half_granules(const uint8_t *kinds, int unit, int lo) {
   size_t bits = 0;
-  for (int i = 0; i < D128; ++i) bits += kinds[i];
+  for (int i = lo; i < lo + 64; ++i) bits += kinds[i];
   size_t gbits = (size_t)granule_bytes(unit) * 8u;
-  size_t ng = (bits + gbits - 1) / gbits;
+  return (bits + gbits - 1) / gbits;
+}
+
+/* first stream bit of row i */
+static size_t row_start_bit(const uint8_t *kinds, int unit, int i) {
+  size_t p = 0;
+  int lo = 0;
+  if (i >= 64) {
+    p = half_granules(kinds, unit, 0) * (size_t)granule_bytes(unit) * 8u;
+    lo = 64;
+  }
+  for (int t = lo; t < i; ++t) p += kinds[t];
+  return p;
+}
+
+size_t or_code_bytes(const uint8_t *kinds, int unit) {
+  size_t ng = half_granules(kinds, unit, 0) + half_granules(kinds, unit, 64);
   return ng * D128 * (size_t)granule_bytes(unit);
 }
 
@@ -341,9 +359,9 @@ void or_encode_block(const uint8_t *kinds, int unit, int scale_mode,
   size_t total = or_block_bytes(kinds, unit, scale_mode);
   memset(block, 0, total);
   for (int j = 0; j < D128; ++j) {
-    size_t p = 0;                       /* stream bit position */
     for (int i = 0; i < D128; ++i) {
       int w = kinds[i];
+      size_t p = row_start_bit(kinds, unit, i);
       uint32_t f = field_of(kinds[i], e[i * D128 + j]);
       for (int t = 0; t < w; ++t, ++p) {
         if ((f >> t) & 1u) block[stream_byte(unit, j, p / 8)] |= (uint8_t)(1u << (p % 8));
@@ -360,9 +378,9 @@ void or_encode_block(const uint8_t *kinds, int unit, int scale_mode,
 void or_decode_block(const uint8_t *kinds, int unit, int scale_mode,
                      const uint8_t *block, uint32_t *e, float *r, float *c) {
   for (int j = 0; j < D128; ++j) {
-    size_t p = 0;
     for (int i = 0; i < D128; ++i) {
       int w = kinds[i];
+      size_t p = row_start_bit(kinds, unit, i);
       uint32_t f = 0;
       for (int t = 0; t < w; ++t, ++p)
         if ((block[stream_byte(unit, j, p / 8)] >> (p % 8)) & 1u) f |= 1u << t;

@@ -17,10 +17,16 @@ enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3 
 struct HeadInfo {
   uint64_t off;         // block offset inside a slot
   uint32_t code_bytes;  // bytes of the code region
-  uint16_t words;       // row units: 32-bit words per column stream
+  uint8_t words0;       // row units: 32-bit words per column for rows 0..63
+  uint8_t words1;       // row units: 32-bit words per column for rows 64..127
   uint8_t kind;         // whole-head units: the head's kind; row units: 0
   uint8_t has_scales;   // 1 when the block stores r (and c)
 };
+
+// Row units: per (head, row) word = bit offset of the row inside its half of
+// the column stream (bits 0..15) | kind (bits 16..23).
+constexpr uint32_t kRowOffMask = 0xFFFFu;
+constexpr int kRowKindShift = 16;
 
 // Everything a launch needs, passed by value as the kernel argument.
 struct LaunchArgs {
@@ -31,8 +37,8 @@ struct LaunchArgs {
   const HeadInfo *heads;
   const int32_t *head_list;   // heads handled by this launch
   int32_t n_list;
-  const uint8_t *row_kind;    // [H*128] (row units)
-  const uint16_t *row_bit;    // [H*128] bit offset of row i in a column stream
+  const uint32_t *row_meta;   // [H*128] (row units), see kRowOffMask
+  int32_t half_words;         // row units: LDS words reserved per column and half
   const float *omega;         // [H*128]
   uint32_t *err;              // device error word
   const int32_t *slots;       // [n] slot of each request / dense entry
@@ -44,7 +50,7 @@ struct LaunchArgs {
 
 struct PoolConfig {
   int unit, gate, scale_mode, fit_iters;
-  int max_words;              // row units: largest words-per-column of any head
+  int max_words;              // row units: largest words-per-column of any half
 };
 
 // Launch every kernel of one mode over `n` requests / dense entries.

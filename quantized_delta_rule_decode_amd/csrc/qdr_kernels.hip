@@ -153,6 +153,10 @@ __device__ __forceinline__ void store_f32(rsrc_t rs, float x, uint32_t voff, uin
   __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(x), rs, voff, soff, 0);
 }
 
+__device__ __forceinline__ void store_u32(rsrc_t rs, uint32_t x, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32((int)x, rs, voff, soff, 0);
+}
+
 // Store one column half (this wave's 64 rows of column j) as 16-byte granules.
 // soff0: byte offset of this wave's first granule row; voff = j*16.
 template <int BITS>
@@ -283,6 +287,7 @@ struct Shared {
   float d[kDim];     // delta, then refit numerator hand-off
   float y[kDim];     // refit denominator hand-off
   float cmax[2][kDim];
+  float qm[kDim];    // row units: largest code of the row's grid (0 for float rows)
   float qb[2];       // each wave's part of sum_i q_i b_i
   float red[2][64][20];
 };
@@ -606,6 +611,377 @@ k_head(const LaunchArgs P) {
 }
 
 // --------------------------------------------------------------------------
+// Row-unit kernel: each key row has its own kind (per-key-channel allocation
+// of the KDA variant, review "STEPQuant: When and Where Errors Matter in
+// Delta-Rule Recurrent State Quantization", Method).  Same thread mapping and
+// arithmetic as k_head; the code stream of this wave's half is staged in LDS
+// (row widths are data, so fields sit at run-time bit offsets) and every
+// per-row branch is wave-uniform (row metadata comes through scalar loads).
+// Padded word slots: LDS reserves half_words + 1 words per column so the
+// straddle read of the last word stays inside the wave's region.
+// --------------------------------------------------------------------------
+template <int MODE, int GATE, int SCALE, int FIT>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+k_rows(const LaunchArgs P) {
+  extern __shared__ uint32_t lds_codes[];
+  __shared__ Shared sh;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int row = 64 * w + l;
+  const int item = blockIdx.x;
+  const int b = item / P.n_list;
+  const int h = P.head_list[item - b * P.n_list];
+  const size_t bh = (size_t)b * P.H + h;
+  const int slot = P.slots[b];
+
+  if (slot < 0 || slot >= P.num_slots) {
+    if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
+    if (MODE == MODE_STEP && w == 0) {
+      float *orow = P.o + bh * kDim;
+      orow[l] = 0.0f;
+      orow[l + 64] = 0.0f;
+    }
+    if (MODE == MODE_UNPACK) {
+      float *dst = P.S_out + bh * kDim * kDim;
+      for (int i = 0; i < 64; ++i) { dst[(64 * w + i) * kDim + l] = 0.0f; dst[(64 * w + i) * kDim + 64 + l] = 0.0f; }
+    }
+    return;
+  }
+  const HeadInfo hi = P.heads[h];
+  const int has_int = hi.has_scales;
+  uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + hi.off;
+  const uint32_t code_bytes = hi.code_bytes;
+  const uint32_t blk_bytes = code_bytes + (has_int ? (SCALE == 0 ? 2u : 1u) * kDim * 4u : 0u);
+  const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(blk, 0, (int)blk_bytes, kRsrcWord3);
+  const int nwords = (w == 0) ? hi.words0 : hi.words1;              // words per column, this half
+  const uint32_t half_off = (w == 0) ? 0u : (uint32_t)hi.words0 * (kDim * 4);
+  const uint32_t r_off = code_bytes, c_off = code_bytes + kDim * 4;
+  uint32_t *codes = lds_codes + (size_t)w * (P.half_words + 1) * kDim;   // [word][column]
+  const uint32_t *__restrict__ meta = P.row_meta + (size_t)h * kDim + 64 * w;
+
+  float S[2][64];
+  float colc[2] = {1.0f, 1.0f};
+
+  // ---------------- stage this half's code words in LDS (1 KiB per wave instruction)
+  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+    const uint32_t bytes = (uint32_t)nwords * (kDim * 4);
+    for (uint32_t off = (uint32_t)l * 16u; off < bytes; off += 1024u) {
+      const uint4 t = load_granule(rs, off, half_off);
+      *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(codes) + off) = t;
+    }
+    // the padding word after the last one (read by straddle-free rows only)
+    codes[nwords * kDim + l] = 0u;
+    codes[nwords * kDim + 64 + l] = 0u;
+  }
+
+  // ---------------- per-row scalars of this lane's row
+  const uint32_t my_meta = P.row_meta[(size_t)h * kDim + row];
+  const int my_kind = (int)(my_meta >> kRowKindShift);
+  const bool my_int = my_kind <= 8;
+  const float my_q = my_int ? (float)((1 << (my_kind - 1)) - 1) : 0.0f;
+  sh.qm[row] = my_q;
+  float a_row = 1.0f;
+  if (MODE == MODE_STEP) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
+  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+    if (my_int) {
+      const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
+      sh.g[row] = a_row * rn_div(r_row, my_q);
+    } else {
+      sh.g[row] = a_row;
+    }
+    if (SCALE == 0 && has_int) {
+      colc[0] = load_f32(rs, (uint32_t)l * 4u, c_off);
+      colc[1] = load_f32(rs, (uint32_t)l * 4u + 256u, c_off);
+    }
+  }
+  float vcol[2] = {0.0f, 0.0f};
+  if (MODE == MODE_STEP) {
+    const float kr = (P.k + bh * kDim)[row];
+    sh.k[row] = kr;
+    sh.b[row] = P.beta[bh] * kr;
+    sh.q[row] = (P.q + bh * kDim)[row];
+    const float *vrow = P.v + bh * kDim;
+    vcol[0] = vrow[l];
+    vcol[1] = vrow[l + 64];
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---------------- restore (and gate), with the balanced first chain
+  float acc1[2] = {0.0f, 0.0f};
+  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+    const float *xsh = (w == 0) ? sh.k : sh.q;
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) {
+      const uint32_t m = meta[ii];
+      const int kind = (int)(m >> kRowKindShift);
+      const uint32_t off = m & kRowOffMask;
+      const uint32_t d = off >> 5, sft = off & 31u;
+      const float g = sh.g[64 * w + ii];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t lo = codes[d * kDim + l + 64 * c];
+        const uint32_t hi2 = codes[(d + 1) * kDim + l + 64 * c];
+        const uint32_t f = __builtin_amdgcn_alignbit(hi2, lo, sft);
+        float sp;
+        if (kind <= 8) {
+          sp = ((float)__builtin_amdgcn_sbfe((int32_t)f, 0, kind) * g) * colc[c];
+        } else if (kind == 16) {
+          sp = g * __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu)));
+        } else {
+          sp = g * __uint_as_float(f);
+        }
+        S[c][ii] = sp;
+      }
+      if (MODE == MODE_STEP) {
+        const float x = xsh[64 * w + ii];
+        acc1[0] = __builtin_fmaf(x, S[0][ii], acc1[0]);
+        acc1[1] = __builtin_fmaf(x, S[1][ii], acc1[1]);
+      }
+      if ((ii & 3) == 3) QDR_FENCE();
+    }
+  }
+
+  if (MODE == MODE_UNPACK) {
+    float *dst = P.S_out + bh * kDim * kDim;
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) {
+      dst[(64 * w + ii) * kDim + l] = S[0][ii];
+      dst[(64 * w + ii) * kDim + 64 + l] = S[1][ii];
+    }
+    return;
+  }
+  if (MODE == MODE_PACK) {
+    const float *src = P.S_in + bh * kDim * kDim;
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) {
+      S[0][ii] = src[(64 * w + ii) * kDim + l];
+      S[1][ii] = src[(64 * w + ii) * kDim + 64 + l];
+    }
+  }
+  if (MODE == MODE_RESET) {
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) { S[0][ii] = 0.0f; S[1][ii] = 0.0f; }
+  }
+
+  // ---------------- delta update (same hand-off as k_head)
+  float oq[2] = {0.0f, 0.0f};
+  float dl[2] = {0.0f, 0.0f};
+  if (MODE == MODE_STEP) {
+    if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
+    const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
+    if (l == 0) sh.qb[w] = qb_part;
+    __syncthreads();
+    float acc2[2] = {0.0f, 0.0f};
+    if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
+    chain_rows(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
+    if (w == 1) {
+      sh.d[l] = vcol[0] - acc2[0];
+      sh.d[l + 64] = vcol[1] - acc2[1];
+      oq[0] = acc1[0]; oq[1] = acc1[1];
+    } else {
+      oq[0] = acc2[0]; oq[1] = acc2[1];
+    }
+    __syncthreads();
+    dl[0] = sh.d[l];
+    dl[1] = sh.d[l + 64];
+#pragma unroll
+    for (int i4 = 0; i4 < 16; ++i4) {
+      const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 4 * i4 + e;
+        S[0][ii] = __builtin_fmaf(bb[e], dl[0], S[0][ii]);
+        S[1][ii] = __builtin_fmaf(bb[e], dl[1], S[1][ii]);
+      }
+      QDR_FENCE();
+    }
+  }
+
+  // ---------------- row factors (integer rows only use them)
+  float r_row = 0.0f, m_row = 0.0f;
+  if (SCALE == 0) {
+    m_row = row_reduce<false>(S, sh.red[w], l) * 0.0078125f;
+    const float nu = rn_div(m_row, (P.omega + (size_t)h * kDim)[row]);
+    r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
+  } else {
+    const float mx = row_reduce<true>(S, sh.red[w], l);
+    r_row = (mx < FLT_MIN) ? 1.0f : mx;
+  }
+  if (!my_int) { r_row = 0.0f; m_row = 0.0f; }
+  sh.ir[row] = my_int ? rn_div(1.0f, r_row) : 0.0f;
+  sh.m[row] = m_row;
+  if (has_int) store_f32(rs, r_row, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
+  __builtin_amdgcn_wave_barrier();
+
+  // Y = S / r in place for integer rows, and the column maximum over them
+  float cm[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int ii = 0; ii < 64; ++ii) {
+    const int kind = (int)(meta[ii] >> kRowKindShift);
+    if (kind <= 8) {
+      const float ir = sh.ir[64 * w + ii];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float y = S[c][ii] * ir;
+        S[c][ii] = y;
+        cm[c] = fmaxf(cm[c], fabsf(y));
+      }
+    }
+    if ((ii & 3) == 3) QDR_FENCE();
+  }
+  float c0[2] = {1.0f, 1.0f};
+  if (SCALE == 0) {
+    sh.cmax[w][l] = cm[0];
+    sh.cmax[w][l + 64] = cm[1];
+  }
+  if (MODE == MODE_STEP && w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
+  __syncthreads();
+  if (SCALE == 0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float mx = fmaxf(sh.cmax[0][l + 64 * c], sh.cmax[1][l + 64 * c]);
+      c0[c] = (mx < FLT_MIN) ? 1.0f : mx;
+    }
+  }
+  float ec[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) ec[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) : 1.0f;
+
+  // ---------------- codes: append each row's field to the column streams;
+  // a finished 32-bit word is stored at once (one coalesced dword per lane
+  // and column), the tail word of the half is zero-padded
+  float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
+  uint32_t acc[2] = {0u, 0u};
+#pragma unroll
+  for (int ii = 0; ii < 64; ++ii) {
+    const uint32_t m = meta[ii];
+    const int kind = (int)(m >> kRowKindShift);
+    const uint32_t off = m & kRowOffMask;
+    const uint32_t d = off >> 5, sft = off & 31u;
+    uint32_t f[2];
+    if (kind <= 8) {
+      const float qm = sh.qm[64 * w + ii];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float t = __builtin_fmaf(S[c][ii], ec[c] * qm, kMagic);
+        f[c] = __float_as_uint(t);
+        if (FIT) {
+          const float zeta = (t - kMagic) * rn_div(1.0f, qm);
+          const float pz = sh.m[64 * w + ii] * zeta;
+          nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
+          dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
+        }
+      }
+    } else if (kind == 16) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) f[c] = (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) f[c] = __float_as_uint(S[c][ii]);
+    }
+    const uint32_t word_off = half_off + d * (kDim * 4);
+    if (kind == 32) {
+      if (sft == 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) { acc[c] = f[c]; store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off); }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], 32u - sft);
+          store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off);
+          acc[c] = f[c];
+        }
+      }
+    } else if (sft + (uint32_t)kind < 32u) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], (uint32_t)kind);
+    } else if (sft + (uint32_t)kind == 32u) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], (uint32_t)kind);
+        store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], 32u - sft);
+        store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off);
+        acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], (uint32_t)kind);
+      }
+    }
+    if ((ii & 3) == 3) QDR_FENCE();
+  }
+  {
+    // tail word: the half's last field ends at bit `end`; if it does not fill
+    // its word, shift the pending bits down and zero-fill the top
+    const uint32_t mlast = meta[63];
+    const uint32_t end = (mlast & kRowOffMask) + (mlast >> kRowKindShift);
+    const uint32_t rem = end & 31u;
+    if (rem != 0u) {
+      const uint32_t word_off = half_off + (end >> 5) * (kDim * 4);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        store_u32(rs, acc[c] >> (32u - rem), (uint32_t)(l + 64 * c) * 4u, word_off);
+    }
+    // whole padding words of the half (granule count rounds up) stay zero
+    for (uint32_t dd = (end + 31u) >> 5; dd < (uint32_t)nwords; ++dd) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        store_u32(rs, 0u, (uint32_t)(l + 64 * c) * 4u, half_off + dd * (kDim * 4));
+    }
+  }
+
+  // ---------------- column factor
+  if (SCALE == 0 && has_int) {
+    if (!FIT) {
+      if (w == 0) {
+        store_f32(rs, c0[0], (uint32_t)l * 4u, c_off);
+        store_f32(rs, c0[1], (uint32_t)l * 4u + 256u, c_off);
+      }
+    } else {
+      if (w == 0) {
+        sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
+        sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];
+      }
+      __syncthreads();
+      if (w == 1) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          // wave 1's own chain started from zero; redo it from wave 0's sums
+          float nn = sh.d[l + 64 * c], dd = sh.y[l + 64 * c];
+#pragma unroll
+          for (int ii = 0; ii < 64; ++ii) {
+            const int kind = (int)(meta[ii] >> kRowKindShift);
+            if (kind <= 8) {
+              const float qm = sh.qm[64 + ii];
+              const float t = __builtin_fmaf(S[c][ii], ec[c] * qm, kMagic);
+              const float zeta = (t - kMagic) * rn_div(1.0f, qm);
+              const float pz = sh.m[64 + ii] * zeta;
+              nn = __builtin_fmaf(pz, S[c][ii], nn);
+              dd = __builtin_fmaf(pz, zeta, dd);
+            }
+          }
+          store_f32(rs, (dd > 0.0f) ? rn_div(nn, dd) : c0[c], (uint32_t)l * 4u + 256u * c, c_off);
+        }
+      }
+    }
+  } else if (SCALE == 0 && FIT) {
+    __syncthreads();   // keep the barrier count uniform across heads of one launch
+  }
+
+  // ---------------- readout
+  if (MODE == MODE_STEP && w == 0) {
+    const float qb_all = sh.qb[0] + sh.qb[1];
+    float *orow = P.o + bh * kDim;
+    orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
+    orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
+  }
+}
+
+// --------------------------------------------------------------------------
 // dispatch
 // --------------------------------------------------------------------------
 namespace {
@@ -655,10 +1031,49 @@ hipError_t launch_heads(const PoolConfig &cfg, LaunchArgs a, int n, const int32_
 
 }  // namespace
 
+template <int MODE>
+hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const int32_t *list, int count,
+                       hipStream_t st) {
+  a.head_list = list;
+  a.n_list = count;
+  a.half_words = cfg.max_words;
+  const dim3 grid((unsigned)((int64_t)n * count)), block(128);
+  if (grid.x == 0) return hipSuccess;
+  const size_t lds = (size_t)2 * (cfg.max_words + 1) * kDim * sizeof(uint32_t);
+  const bool dual = cfg.scale_mode == 0, fit = cfg.fit_iters > 0, diag = cfg.gate == 1;
+  if (lds > 65536) {   // pools with FP32 rows: allow the larger dynamic LDS
+    const void *fns[6] = {(const void *)k_rows<MODE, 1, 1, 0>, (const void *)k_rows<MODE, 0, 1, 0>,
+                          (const void *)k_rows<MODE, 1, 0, 1>, (const void *)k_rows<MODE, 0, 0, 1>,
+                          (const void *)k_rows<MODE, 1, 0, 0>, (const void *)k_rows<MODE, 0, 0, 0>};
+    for (const void *f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (!dual) {
+    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 1, 0>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((k_rows<MODE, 0, 1, 0>), grid, block, lds, st, a);
+  } else if (fit) {
+    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 1>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 1>), grid, block, lds, st, a);
+  } else {
+    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 0>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 0>), grid, block, lds, st, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const int32_t *const *kind_lists,
                       const int32_t *kind_counts, int mode, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  if (cfg.unit != 0) return hipErrorNotSupported;
+  if (cfg.unit != 0) {
+    switch (mode) {
+      case MODE_STEP: return launch_rows<MODE_STEP>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
+      case MODE_PACK: return launch_rows<MODE_PACK>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
+      case MODE_UNPACK: return launch_rows<MODE_UNPACK>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
+      default: return launch_rows<MODE_RESET>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
+    }
+  }
   switch (mode) {
     case MODE_STEP: return launch_heads<MODE_STEP>(cfg, args, n, kind_lists, kind_counts, stream);
     case MODE_PACK: return launch_heads<MODE_PACK>(cfg, args, n, kind_lists, kind_counts, stream);

@@ -61,8 +61,8 @@ bool debug_slots() {
 struct HostLayout {
   std::vector<uint64_t> head_off;
   std::vector<uint32_t> head_bytes, code_bytes;
-  std::vector<uint16_t> words;        // row units: words per column
-  std::vector<uint16_t> row_bit;      // row units: [H*128]
+  std::vector<uint8_t> words0, words1; // row units: words per column and half
+  std::vector<uint32_t> row_meta;     // row units: [H*128]
   std::vector<uint8_t> has_scales;
   uint64_t slot_stride = 0;
   int max_words = 0;
@@ -98,37 +98,49 @@ qdr_status check_desc(const qdr_pool_desc *d) {
   return QDR_OK;
 }
 
+// Block layout (see include/qdr.h): the code stream of a column holds rows
+// 0..127 as b-bit fields; rows 0..63 and rows 64..127 each fill whole
+// granules (16 B for whole-head units, 4 B for row units), granule g of
+// column j at byte (g*128 + j)*G; then r (and c) when there are integer rows;
+// blocks padded to 256 B.
 void build_layout(const qdr_pool_desc *d, HostLayout &L) {
   const int H = d->num_heads;
   L.head_off.resize(H);
   L.head_bytes.resize(H);
   L.code_bytes.resize(H);
-  L.words.resize(H);
+  L.words0.resize(H);
+  L.words1.resize(H);
   L.has_scales.resize(H);
-  if (d->unit == QDR_UNIT_ROW) L.row_bit.resize((size_t)H * QDR_DIM);
+  if (d->unit == QDR_UNIT_ROW) L.row_meta.resize((size_t)H * QDR_DIM);
   uint64_t off = 0;
   double bits = 0;
   L.max_words = 0;
+  const uint64_t G = d->unit == QDR_UNIT_HEAD ? 16 : 4;
   for (int h = 0; h < H; ++h) {
-    uint64_t colbits = 0;
+    uint64_t ng = 0;
     bool any_int = false;
-    for (int i = 0; i < QDR_DIM; ++i) {
-      const int k = d->unit == QDR_UNIT_HEAD ? d->kinds[h] : d->kinds[(size_t)h * QDR_DIM + i];
-      if (d->unit == QDR_UNIT_ROW) L.row_bit[(size_t)h * QDR_DIM + i] = (uint16_t)colbits;
-      colbits += (uint64_t)k;
-      any_int = any_int || is_int_kind(k);
+    for (int half = 0; half < 2; ++half) {
+      uint64_t hbits = 0;
+      for (int i = 64 * half; i < 64 * half + 64; ++i) {
+        const int k = d->unit == QDR_UNIT_HEAD ? d->kinds[h] : d->kinds[(size_t)h * QDR_DIM + i];
+        if (d->unit == QDR_UNIT_ROW)
+          L.row_meta[(size_t)h * QDR_DIM + i] = (uint32_t)hbits | ((uint32_t)k << qdr::kRowKindShift);
+        hbits += (uint64_t)k;
+        any_int = any_int || is_int_kind(k);
+      }
+      const uint64_t hg = (hbits + 8 * G - 1) / (8 * G);
+      ng += hg;
+      const int words = (int)(hg * G / 4);
+      (half == 0 ? L.words0 : L.words1)[h] = (uint8_t)words;
+      if (words > L.max_words) L.max_words = words;
     }
-    const uint64_t G = d->unit == QDR_UNIT_HEAD ? 16 : 4;
-    const uint64_t ng = (colbits + 8 * G - 1) / (8 * G);
     const uint64_t code = ng * QDR_DIM * G;
     const uint64_t scales = any_int ? (d->scale_mode == QDR_SCALE_DUAL ? 2 * QDR_DIM * 4 : QDR_DIM * 4) : 0;
     const uint64_t blk = (code + scales + 255) / 256 * 256;
     L.head_off[h] = off;
     L.head_bytes[h] = (uint32_t)blk;
     L.code_bytes[h] = (uint32_t)code;
-    L.words[h] = (uint16_t)(code / QDR_DIM / 4);
     L.has_scales[h] = any_int ? 1 : 0;
-    if (L.words[h] > L.max_words) L.max_words = L.words[h];
     off += blk;
     bits += 8.0 * (double)blk;
   }
@@ -148,8 +160,7 @@ struct qdr_pool {
   uint8_t *base = nullptr;
   bool owns_base = false;
   qdr::HeadInfo *d_heads = nullptr;
-  uint8_t *d_row_kind = nullptr;
-  uint16_t *d_row_bit = nullptr;
+  uint32_t *d_row_meta = nullptr;
   float *d_omega = nullptr;
   uint32_t *d_err = nullptr;
   int32_t *d_lists[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
@@ -171,8 +182,7 @@ void free_pool(qdr_pool *p) {
   if (!p) return;
   if (p->owns_base && p->base) (void)hipFree(p->base);
   (void)hipFree(p->d_heads);
-  (void)hipFree(p->d_row_kind);
-  (void)hipFree(p->d_row_bit);
+  (void)hipFree(p->d_row_meta);
   (void)hipFree(p->d_omega);
   (void)hipFree(p->d_err);
   for (auto &l : p->d_lists) (void)hipFree(l);
@@ -186,8 +196,7 @@ qdr::LaunchArgs base_args(const qdr_pool *p) {
   a.num_slots = p->desc.num_slots;
   a.H = p->desc.num_heads;
   a.heads = p->d_heads;
-  a.row_kind = p->d_row_kind;
-  a.row_bit = p->d_row_bit;
+  a.row_meta = p->d_row_meta;
   a.omega = p->d_omega;
   a.err = p->d_err;
   return a;
@@ -275,7 +284,8 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
   for (int h = 0; h < desc->num_heads; ++h) {
     hi[h].off = p->L.head_off[h];
     hi[h].code_bytes = p->L.code_bytes[h];
-    hi[h].words = p->L.words[h];
+    hi[h].words0 = p->L.words0[h];
+    hi[h].words1 = p->L.words1[h];
     hi[h].kind = desc->unit == QDR_UNIT_HEAD ? p->kinds[h] : 0;
     hi[h].has_scales = p->L.has_scales[h];
     if (desc->unit == QDR_UNIT_HEAD) lists[kind_index(p->kinds[h])].push_back(h);
@@ -285,8 +295,7 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
   if (e == hipSuccess) e = upload(&p->d_heads, hi.data(), hi.size());
   if (e == hipSuccess) e = upload(&p->d_omega, p->omega.data(), p->omega.size());
   if (e == hipSuccess && desc->unit == QDR_UNIT_ROW) {
-    e = upload(&p->d_row_kind, p->kinds.data(), p->kinds.size());
-    if (e == hipSuccess) e = upload(&p->d_row_bit, p->L.row_bit.data(), p->L.row_bit.size());
+    e = upload(&p->d_row_meta, p->L.row_meta.data(), p->L.row_meta.size());
   }
   for (int i = 0; i < 6 && e == hipSuccess; ++i) {
     p->list_count[i] = (int32_t)lists[i].size();

@@ -257,3 +257,78 @@ def test_config1_trajectory(torch_dev, orc):
 def test_config2_trajectory(torch_dev, orc):
     worst, excused = trajectory(torch_dev, orc, 2, 48)
     assert worst <= 1e-4
+
+
+# ----------------------------------------------------------------- row units (KDA)
+def row_kinds(name, H, seed=0):
+    g = np.random.default_rng(seed)
+    if name == "kda_mix":
+        k = g.choice([2, 4, 6, 8], size=(H, D), p=[0.3, 0.4, 0.2, 0.1])
+        k[g.random((H, D)) < 0.03] = 16
+    elif name == "fp32_rows":
+        k = g.choice([2, 4, 6, 8, 16, 32], size=(H, D))
+    elif name == "float_only_head":
+        k = g.choice([2, 6, 8], size=(H, D))
+        k[1] = 16
+    else:   # odd widths that straddle words at every position
+        k = np.tile(np.array([6, 2, 6, 6, 4, 8, 6, 2], np.uint8), (H, D // 8))
+    return np.ascontiguousarray(k.reshape(-1), np.uint8)
+
+
+ROW_SETS = ["kda_mix", "fp32_rows", "float_only_head", "straddle"]
+
+
+@pytest.mark.parametrize("name", ROW_SETS)
+@pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
+def test_rows_pack_unpack_parity(torch_dev, orc, name, scale, fit):
+    torch = torch_dev
+    H = 3
+    kinds = row_kinds(name, H, 5)
+    omega = np.random.default_rng(6).lognormal(0, 1, (H, D)).astype(np.float32)
+    dev, ref = make_pair(orc, 4, kinds, omega, unit=1, gate=1, scale=scale, fit=fit)
+    slots = np.array([2, 0, 3], np.int32)
+    S = edge_states(13, 3, H)
+    dev.qdr_pack(t_(torch, slots), t_(torch, S))
+    ref.pack(slots, S)
+    torch.cuda.synchronize()
+    rep = parity.StepReport()
+    parity.compare_pool(orc, ref, dev, slots, lambda b, h: S[b, h], rep, resync=False)
+    parity.assert_step_ok(rep, f"rows pack {name} scale={scale} fit={fit}")
+    assert rep.blocks_mismatched == 0
+    # restore from the (identical) packed bytes
+    out = torch.full((3, H, D, D), 5.0, dtype=torch.float32, device="cuda")
+    us = np.array([3, -1, 2], np.int32)
+    dev.qdr_unpack(t_(torch, us), out)
+    X_ref = ref.unpack(us)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), X_ref.view(np.uint32))
+    # zero state
+    dev.qdr_slot_reset(t_(torch, np.array([1], np.int32)))
+    ref.pack(np.array([1], np.int32), np.zeros((1, H, D, D), np.float32))
+    assert np.array_equal(dev.qdr_read_raw(1), ref.mem[ref.slot_stride:2 * ref.slot_stride])
+
+
+@pytest.mark.parametrize("name", ROW_SETS)
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
+def test_rows_step_parity(torch_dev, orc, name, gate, scale, fit):
+    torch = torch_dev
+    H = 3
+    kinds = row_kinds(name, H, 7)
+    omega = np.random.default_rng(8).lognormal(0, 1, (H, D)).astype(np.float32)
+    dev, ref = make_pair(orc, 5, kinds, omega, unit=1, gate=gate, scale=scale, fit=fit)
+    S = edge_states(17, 5, H)
+    all_slots = np.arange(5, dtype=np.int32)
+    dev.qdr_pack(t_(torch, all_slots), t_(torch, S))
+    ref.pack(all_slots, S)
+    slots = np.array([3, -1, 1, 4], np.int32)
+    inputs = random_inputs(18, slots.size, H, gate == 1)
+    rep, o_dev, o_ref, bad = run_step_pair(torch, orc, dev, ref, slots, inputs)
+    parity.assert_step_ok(rep, f"rows step {name} gate={gate} scale={scale} fit={fit}")
+    assert bad == 0 and np.all(o_dev[1] == 0)
+    for s in (0, 2):
+        assert np.array_equal(dev.qdr_read_raw(s), ref.mem[s * ref.slot_stride:(s + 1) * ref.slot_stride])
+
+
+def test_config3_trajectory(torch_dev, orc):
+    worst, excused = trajectory(torch_dev, orc, 3, 12)
+    assert worst <= 1e-4

@@ -15,26 +15,31 @@ D = 128
 def ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c):
     G = 16 if unit == 0 else 4
     widths = [int(k) for k in kinds]
-    total_bits = sum(widths)
     gbits = 8 * G
-    ng = (total_bits + gbits - 1) // gbits
+    ng0 = (sum(widths[:64]) + gbits - 1) // gbits
+    ng1 = (sum(widths[64:]) + gbits - 1) // gbits
+    ng = ng0 + ng1
     code_bytes = ng * D * G
     has_int = any(w <= 8 for w in widths)
     sbytes = (2 * D * 4 if scale_mode == 0 else D * 4) if has_int else 0
     size = (code_bytes + sbytes + 255) // 256 * 256
     out = bytearray(size)
     for j in range(D):
-        stream = 0
-        pos = 0
-        for i, w in enumerate(widths):
-            if w <= 8:
-                field = int(codes[i, j]) % (1 << w)     # b-bit two's complement
-            else:
-                field = int(fp_bits[i, j])
-            assert 0 <= field < (1 << w)
-            stream |= field << pos
-            pos += w
-        raw = stream.to_bytes(ng * G, "little")
+        halves = []
+        for lo in (0, 64):
+            stream = 0
+            pos = 0
+            for i in range(lo, lo + 64):
+                w = widths[i]
+                if w <= 8:
+                    field = int(codes[i, j]) % (1 << w)     # b-bit two's complement
+                else:
+                    field = int(fp_bits[i, j])
+                assert 0 <= field < (1 << w)
+                stream |= field << pos
+                pos += w
+            halves.append(stream)
+        raw = halves[0].to_bytes(ng0 * G, "little") + halves[1].to_bytes(ng1 * G, "little")
         for n, byte in enumerate(raw):
             out[((n // G) * D + j) * G + n % G] = byte
     if has_int:
@@ -70,6 +75,7 @@ KIND_SETS = {
     "mixed": [2, 4, 6, 8, 16, 6, 4, 2] * 16,
     "mixed_fp32": [32, 2, 2, 6] * 32,
     "odd": [6] * 127 + [2],
+    "odd_halves": [6] * 63 + [2] + [16] * 3 + [6] * 61,
 }
 
 
@@ -108,9 +114,11 @@ def test_block_sizes(orc):
     assert orc.block_bytes(np.full(D, 16, np.uint8), 0, 0) == 32768
     # an FP32 head is the uncompressed 128 x 128 fp32 state: 64 KiB
     assert orc.block_bytes(np.full(D, 32, np.uint8), 0, 0) == 65536
-    # row units pad each column stream to whole 32-bit words
-    k = np.array([6] * 127 + [2], np.uint8)     # 764 bits -> 768
+    # row units pad each half of a column stream to whole 32-bit words
+    k = np.array([6] * 127 + [2], np.uint8)     # 384 + 380 bits -> 12 + 12 words
     assert orc.code_bytes(k, 1) == 24 * 4 * D
+    k = np.array([6] * 63 + [2] + [4] * 64, np.uint8)   # 380 -> 12 words, 256 -> 8 words
+    assert orc.code_bytes(k, 1) == 20 * 4 * D
 
 
 def test_pages_state_bytes(orc):

@@ -623,7 +623,7 @@ k_head(const LaunchArgs P) {
 template <int MODE, int GATE, int SCALE, int FIT>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 k_rows(const LaunchArgs P) {
-  extern __shared__ uint32_t lds_codes[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds_codes[];   // 16-byte aligned: staged with ds_write_b128
   __shared__ Shared sh;
 
   const int tid = threadIdx.x;
@@ -726,7 +726,11 @@ k_rows(const LaunchArgs P) {
         const uint32_t f = __builtin_amdgcn_alignbit(hi2, lo, sft);
         float sp;
         if (kind <= 8) {
-          sp = ((float)__builtin_amdgcn_sbfe((int32_t)f, 0, kind) * g) * colc[c];
+          // sign-extend the low `kind` bits with two shifts; the bfe builtin
+          // with a run-time width is mis-typed as unsigned by the compiler
+          const uint32_t up = 32u - (uint32_t)kind;
+          const int32_t z = (int32_t)(f << up) >> up;
+          sp = ((float)z * g) * colc[c];
         } else if (kind == 16) {
           sp = g * __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu)));
         } else {

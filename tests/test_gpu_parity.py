@@ -29,9 +29,10 @@ def t_(torch, x, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
-def edge_states(seed, n, H):
+def edge_states(seed, n, H, fp16_rows=None):
     """Random outlier states plus degenerate heads: zero head, zero rows,
-    zero columns, tiny magnitudes, large dynamic range."""
+    zero columns, tiny magnitudes, large dynamic range.  fp16_rows (bool
+    [H,128]) marks pivot rows, which must stay inside the binary16 range."""
     S = synth.random_state(seed, n, H)
     if H >= 4:
         S[0, 0] = 0.0
@@ -39,8 +40,10 @@ def edge_states(seed, n, H):
         S[0, 2, :, 17] = 0.0
         S[0, 2, :, 100] = 0.0
         S[-1, 3] *= np.float32(1e-30)
-    if n > 1 and H >= 2:
+    if n > 1 and H >= 2 and (fp16_rows is None or not fp16_rows[1, 3]):
         S[1, 1, 3] *= np.float32(1e6)
+    if fp16_rows is not None:
+        S = np.where(fp16_rows[None, :, :, None], np.clip(S, -6e4, 6e4), S).astype(np.float32)
     return S
 
 
@@ -287,7 +290,7 @@ def test_rows_pack_unpack_parity(torch_dev, orc, name, scale, fit):
     omega = np.random.default_rng(6).lognormal(0, 1, (H, D)).astype(np.float32)
     dev, ref = make_pair(orc, 4, kinds, omega, unit=1, gate=1, scale=scale, fit=fit)
     slots = np.array([2, 0, 3], np.int32)
-    S = edge_states(13, 3, H)
+    S = edge_states(13, 3, H, kinds.reshape(H, D) == 16)
     dev.qdr_pack(t_(torch, slots), t_(torch, S))
     ref.pack(slots, S)
     torch.cuda.synchronize()
@@ -316,7 +319,7 @@ def test_rows_step_parity(torch_dev, orc, name, gate, scale, fit):
     kinds = row_kinds(name, H, 7)
     omega = np.random.default_rng(8).lognormal(0, 1, (H, D)).astype(np.float32)
     dev, ref = make_pair(orc, 5, kinds, omega, unit=1, gate=gate, scale=scale, fit=fit)
-    S = edge_states(17, 5, H)
+    S = edge_states(17, 5, H, kinds.reshape(H, D) == 16)
     all_slots = np.arange(5, dtype=np.int32)
     dev.qdr_pack(t_(torch, all_slots), t_(torch, S))
     ref.pack(all_slots, S)

@@ -29,19 +29,18 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "state-update steps/s (requests x heads) at B=512, 6-bit; achieved HBM GB/s"
 
 
-def algorithmic_bytes(cfg, pool, kinds_per_head) -> int:
-    """Bytes the step must move, per the method: codes and scales read and
-    written once, q/k/v read, beta and the gate read, o written."""
+def algorithmic_bytes(cfg, tables) -> int:
+    """Bytes one step must move by the method's own accounting: every code
+    (b bits per state value of its row, no layout padding) and every scale
+    read and written once, q/k/v, beta and the gate read, o written."""
     H = cfg.H
-    per_req = 0
-    for h in range(H):
-        code = int(pool.code_bytes[h])
-        scales = 0
-        if kinds_per_head[h] <= 8:
-            scales = 2 * 128 * 4 if cfg.scale_mode == 0 else 128 * 4
-        per_req += 2 * code + 2 * scales
+    kinds = np.asarray(tables["kinds"], np.int64)
+    rows = np.repeat(kinds, 128).reshape(H, 128) if cfg.unit == 0 else kinds.reshape(H, 128)
+    code = rows.sum(axis=1) * 128 // 8                       # bytes per head
+    has_int = (rows <= 8).any(axis=1)
+    scales = np.where(has_int, (2 if cfg.scale_mode == 0 else 1) * 128 * 4, 0)
     gate_bytes = 4 if cfg.gate == 0 else 4 * 128
-    per_req += H * (3 * 128 * 4 + 4 + gate_bytes + 128 * 4)
+    per_req = int((2 * code + 2 * scales).sum()) + H * (3 * 128 * 4 + 4 + gate_bytes + 128 * 4)
     return per_req * cfg.B
 
 
@@ -127,10 +126,7 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
     assert pool.qdr_poll_device_error() == 0
 
-    kinds_h = tables["kinds"] if cfg.unit == 0 else None
-    if kinds_h is None:
-        kinds_h = np.full(cfg.H, 4, np.uint8)
-    nbytes = algorithmic_bytes(cfg, pool, kinds_h)
+    nbytes = algorithmic_bytes(cfg, tables)
     head_steps = cfg.B * cfg.H
     achieved = nbytes / (gpu_ms * 1e-3) / 1e9
     value = head_steps / (gpu_ms * 1e-3)

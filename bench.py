@@ -44,6 +44,24 @@ def algorithmic_bytes(cfg, tables) -> int:
     return per_req * cfg.B
 
 
+def measured_traffic(cid: int):
+    """HBM bytes per step from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (scaled by a plain-copy calibration), or None when the kernel source
+    has changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "quantized_delta_rule_decode_amd", "csrc", "qdr_kernels.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(f"config{cid}")
+    if rec.get("kernel_source_sha256_16") != sha or entry is None:
+        return None
+    return entry["fetch_bytes_per_step"] + entry["write_bytes_per_step"]
+
+
 def cpu_baseline(cfg, tables, requests: int, threads: int):
     """The CPU oracle, as it stands, on `requests` requests x all heads."""
     from oracle import oracle as orc
@@ -127,6 +145,7 @@ def main():
     assert pool.qdr_poll_device_error() == 0
 
     nbytes = algorithmic_bytes(cfg, tables)
+    traffic = measured_traffic(cfg.cid)
     head_steps = cfg.B * cfg.H
     achieved = nbytes / (gpu_ms * 1e-3) / 1e9
     value = head_steps / (gpu_ms * 1e-3)
@@ -158,7 +177,10 @@ def main():
         "achieved_GBps": achieved,
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None},
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "unit_of_work": "one qdr_decode_step = one kernel launch per storage kind, back to back "
+                                     "on one stream; achieved = algorithmic bytes / step time",
+                     "traffic_over_algorithmic": None if traffic is None else traffic / nbytes},
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "setup_s": setup_s,

@@ -288,6 +288,7 @@ struct Shared {
   float y[kDim];     // refit denominator hand-off
   float cmax[2][kDim];
   float qm[kDim];    // row units: largest code of the row's grid (0 for float rows)
+  float iq[kDim];    // row units: 1/qm (0 for float rows)
   float qb[2];       // each wave's part of sum_i q_i b_i
   float red[2][64][20];
 };
@@ -614,11 +615,18 @@ k_head(const LaunchArgs P) {
 // Row-unit kernel: each key row has its own kind (per-key-channel allocation
 // of the KDA variant, review "STEPQuant: When and Where Errors Matter in
 // Delta-Rule Recurrent State Quantization", Method).  Same thread mapping and
-// arithmetic as k_head; the code stream of this wave's half is staged in LDS
-// (row widths are data, so fields sit at run-time bit offsets) and every
-// per-row branch is wave-uniform (row metadata comes through scalar loads).
-// Padded word slots: LDS reserves half_words + 1 words per column so the
-// straddle read of the last word stays inside the wave's region.
+// arithmetic as k_head.  Row widths are data, so:
+//   * each wave stages its half of the column streams in LDS and reads a
+//     row's field at a run-time bit offset (funnel shift of two words);
+//   * row metadata (bit offset | kind) is read back per row with v_readlane,
+//     so it is wave-uniform (SGPR) and every branch on it is scalar;
+//   * integer rows run straight-line code; the rare FP16/FP32 rows patch
+//     their values in a uniform branch;
+//   * repacking ORs each field into a zeroed LDS copy of the half
+//     (ds_or_b32 on the one or two words it touches), which is then stored
+//     with 16-byte coalesced writes: no per-row flush logic.
+// LDS reserves half_words + 1 words per column so the second word of a
+// field's funnel shift stays inside the wave's region.
 // --------------------------------------------------------------------------
 template <int MODE, int GATE, int SCALE, int FIT>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
@@ -657,31 +665,33 @@ k_rows(const LaunchArgs P) {
   const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(blk, 0, (int)blk_bytes, kRsrcWord3);
   const int nwords = (w == 0) ? hi.words0 : hi.words1;              // words per column, this half
   const uint32_t half_off = (w == 0) ? 0u : (uint32_t)hi.words0 * (kDim * 4);
+  const uint32_t half_bytes = (uint32_t)nwords * (kDim * 4);
   const uint32_t r_off = code_bytes, c_off = code_bytes + kDim * 4;
   uint32_t *codes = lds_codes + (size_t)w * (P.half_words + 1) * kDim;   // [word][column]
-  const uint32_t *__restrict__ meta = P.row_meta + (size_t)h * kDim + 64 * w;
+  uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
+
+  // row metadata of this wave's 64 rows: lane l holds row 64w+l's word, and
+  // row ii's word is read back with v_readlane (an SGPR value)
+  const uint32_t meta_lane = P.row_meta[(size_t)h * kDim + 64 * w + l];
+#define ROW_META(ii) ((uint32_t)__builtin_amdgcn_readlane((int)meta_lane, (ii)))
 
   float S[2][64];
   float colc[2] = {1.0f, 1.0f};
 
   // ---------------- stage this half's code words in LDS (1 KiB per wave instruction)
   if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
-    const uint32_t bytes = (uint32_t)nwords * (kDim * 4);
-    for (uint32_t off = (uint32_t)l * 16u; off < bytes; off += 1024u) {
-      const uint4 t = load_granule(rs, off, half_off);
-      *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(codes) + off) = t;
-    }
-    // the padding word after the last one (read by straddle-free rows only)
+    for (uint32_t off = (uint32_t)l * 16u; off < half_bytes; off += 1024u)
+      *reinterpret_cast<uint4 *>(codes8 + off) = load_granule(rs, off, half_off);
     codes[nwords * kDim + l] = 0u;
     codes[nwords * kDim + 64 + l] = 0u;
   }
 
   // ---------------- per-row scalars of this lane's row
-  const uint32_t my_meta = P.row_meta[(size_t)h * kDim + row];
-  const int my_kind = (int)(my_meta >> kRowKindShift);
+  const int my_kind = (int)(meta_lane >> kRowKindShift);
   const bool my_int = my_kind <= 8;
   const float my_q = my_int ? (float)((1 << (my_kind - 1)) - 1) : 0.0f;
   sh.qm[row] = my_q;
+  if (FIT) sh.iq[row] = my_int ? rn_div(1.0f, my_q) : 0.0f;
   float a_row = 1.0f;
   if (MODE == MODE_STEP) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
   if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
@@ -713,37 +723,42 @@ k_rows(const LaunchArgs P) {
   if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
     const float *xsh = (w == 0) ? sh.k : sh.q;
 #pragma unroll
-    for (int ii = 0; ii < 64; ++ii) {
-      const uint32_t m = meta[ii];
-      const int kind = (int)(m >> kRowKindShift);
-      const uint32_t off = m & kRowOffMask;
-      const uint32_t d = off >> 5, sft = off & 31u;
-      const float g = sh.g[64 * w + ii];
+    for (int i4 = 0; i4 < 16; ++i4) {
+      const float4 g4 = lds4(&sh.g[64 * w + 4 * i4]);
+      float4 x4 = {0, 0, 0, 0};
+      if (MODE == MODE_STEP) x4 = lds4(&xsh[64 * w + 4 * i4]);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+      const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint32_t lo = codes[d * kDim + l + 64 * c];
-        const uint32_t hi2 = codes[(d + 1) * kDim + l + 64 * c];
-        const uint32_t f = __builtin_amdgcn_alignbit(hi2, lo, sft);
-        float sp;
-        if (kind <= 8) {
-          // sign-extend the low `kind` bits with two shifts; the bfe builtin
-          // with a run-time width is mis-typed as unsigned by the compiler
-          const uint32_t up = 32u - (uint32_t)kind;
-          const int32_t z = (int32_t)(f << up) >> up;
-          sp = ((float)z * g) * colc[c];
-        } else if (kind == 16) {
-          sp = g * __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu)));
-        } else {
-          sp = g * __uint_as_float(f);
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 4 * i4 + e;
+        const uint32_t m = ROW_META(ii);
+        const uint32_t kind = m >> kRowKindShift;
+        const uint32_t off = m & kRowOffMask;
+        const uint32_t d = off >> 5, sft = off & 31u;
+        const uint32_t up = (32u - kind) & 31u;     // integer rows: 24..30
+        uint32_t f[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t lo = codes[d * kDim + l + 64 * c];
+          const uint32_t hi2 = codes[(d + 1) * kDim + l + 64 * c];
+          f[c] = __builtin_amdgcn_alignbit(hi2, lo, sft);
+          // integer code: sign-extend the low `kind` bits with two shifts
+          const int32_t z = (int32_t)(f[c] << up) >> up;
+          S[c][ii] = ((float)z * gg[e]) * colc[c];
         }
-        S[c][ii] = sp;
+        if (kind > 8u) {   // pivot rows (rare): the stored value itself
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            S[c][ii] = gg[e] * (kind == 16u ? __half2float(__ushort_as_half((unsigned short)(f[c] & 0xFFFFu)))
+                                            : __uint_as_float(f[c]));
+        }
+        if (MODE == MODE_STEP) {
+          acc1[0] = __builtin_fmaf(xx[e], S[0][ii], acc1[0]);
+          acc1[1] = __builtin_fmaf(xx[e], S[1][ii], acc1[1]);
+        }
       }
-      if (MODE == MODE_STEP) {
-        const float x = xsh[64 * w + ii];
-        acc1[0] = __builtin_fmaf(x, S[0][ii], acc1[0]);
-        acc1[1] = __builtin_fmaf(x, S[1][ii], acc1[1]);
-      }
-      if ((ii & 3) == 3) QDR_FENCE();
+      QDR_FENCE();
     }
   }
 
@@ -804,6 +819,11 @@ k_rows(const LaunchArgs P) {
     }
   }
 
+  // the staged copy is reused as the output buffer: clear it while the row
+  // factors are computed
+  for (uint32_t off = (uint32_t)l * 16u; off < half_bytes + kDim * 4u; off += 1024u)
+    *reinterpret_cast<uint4 *>(codes8 + off) = make_uint4(0u, 0u, 0u, 0u);
+
   // ---------------- row factors (integer rows only use them)
   float r_row = 0.0f, m_row = 0.0f;
   if (SCALE == 0) {
@@ -815,26 +835,34 @@ k_rows(const LaunchArgs P) {
     r_row = (mx < FLT_MIN) ? 1.0f : mx;
   }
   if (!my_int) { r_row = 0.0f; m_row = 0.0f; }
-  sh.ir[row] = my_int ? rn_div(1.0f, r_row) : 0.0f;
+  // pivot rows keep their values through the Y pass (factor 1) and are
+  // excluded from the column maximum (flag 0)
+  sh.ir[row] = my_int ? rn_div(1.0f, r_row) : 1.0f;
   sh.m[row] = m_row;
   if (has_int) store_f32(rs, r_row, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
   __builtin_amdgcn_wave_barrier();
 
-  // Y = S / r in place for integer rows, and the column maximum over them
+  // Y = S / r in place (integer rows), and the column maximum over integer rows
   float cm[2] = {0.0f, 0.0f};
 #pragma unroll
-  for (int ii = 0; ii < 64; ++ii) {
-    const int kind = (int)(meta[ii] >> kRowKindShift);
-    if (kind <= 8) {
-      const float ir = sh.ir[64 * w + ii];
+  for (int i4 = 0; i4 < 16; ++i4) {
+    const float4 r4 = lds4(&sh.ir[64 * w + 4 * i4]);
+    const float4 q4 = lds4(&sh.qm[64 * w + 4 * i4]);
+    const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+    const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ii = 4 * i4 + e;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const float y = S[c][ii] * ir;
+        const float y = S[c][ii] * rr[e];
         S[c][ii] = y;
-        cm[c] = fmaxf(cm[c], fabsf(y));
+        // qm is 0 exactly for pivot rows: max(cm, |y| * 0) leaves cm unchanged
+        // (|y| is finite for finite states), so no branch is needed
+        cm[c] = fmaxf(cm[c], (qq[e] > 0.0f) ? fabsf(y) : 0.0f);
       }
     }
-    if ((ii & 3) == 3) QDR_FENCE();
+    QDR_FENCE();
   }
   float c0[2] = {1.0f, 1.0f};
   if (SCALE == 0) {
@@ -854,88 +882,59 @@ k_rows(const LaunchArgs P) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) ec[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) : 1.0f;
 
-  // ---------------- codes: append each row's field to the column streams;
-  // a finished 32-bit word is stored at once (one coalesced dword per lane
-  // and column), the tail word of the half is zero-padded
+  // ---------------- codes: OR each row's field into the cleared LDS words
   float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
-  uint32_t acc[2] = {0u, 0u};
 #pragma unroll
-  for (int ii = 0; ii < 64; ++ii) {
-    const uint32_t m = meta[ii];
-    const int kind = (int)(m >> kRowKindShift);
-    const uint32_t off = m & kRowOffMask;
-    const uint32_t d = off >> 5, sft = off & 31u;
-    uint32_t f[2];
-    if (kind <= 8) {
-      const float qm = sh.qm[64 * w + ii];
+  for (int i4 = 0; i4 < 16; ++i4) {
+    const float4 q4 = lds4(&sh.qm[64 * w + 4 * i4]);
+    const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+    float4 m4 = {0, 0, 0, 0}, iq4 = {0, 0, 0, 0};
+    if (FIT) { m4 = lds4(&sh.m[64 * w + 4 * i4]); iq4 = lds4(&sh.iq[64 * w + 4 * i4]); }
+    const float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+    const float iqq[4] = {iq4.x, iq4.y, iq4.z, iq4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ii = 4 * i4 + e;
+      const uint32_t m = ROW_META(ii);
+      const uint32_t kind = m >> kRowKindShift;
+      const uint32_t off = m & kRowOffMask;
+      const uint32_t d = off >> 5, sft = off & 31u;
+      uint32_t f[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const float t = __builtin_fmaf(S[c][ii], ec[c] * qm, kMagic);
+        const float t = __builtin_fmaf(S[c][ii], ec[c] * qq[e], kMagic);
         f[c] = __float_as_uint(t);
         if (FIT) {
-          const float zeta = (t - kMagic) * rn_div(1.0f, qm);
-          const float pz = sh.m[64 * w + ii] * zeta;
+          // pivot rows: 1/q is stored as 0, so they add exact zeros
+          const float zeta = (t - kMagic) * iqq[e];
+          const float pz = mm[e] * zeta;
           nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
           dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
         }
       }
-    } else if (kind == 16) {
+      if (kind > 8u) {   // pivot rows (rare)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) f[c] = (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) f[c] = __float_as_uint(S[c][ii]);
-    }
-    const uint32_t word_off = half_off + d * (kDim * 4);
-    if (kind == 32) {
-      if (sft == 0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) { acc[c] = f[c]; store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off); }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], 32u - sft);
-          store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off);
-          acc[c] = f[c];
-        }
+        for (int c = 0; c < 2; ++c)
+          f[c] = (kind == 16u) ? (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])))
+                               : __float_as_uint(S[c][ii]);
       }
-    } else if (sft + (uint32_t)kind < 32u) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], (uint32_t)kind);
-    } else if (sft + (uint32_t)kind == 32u) {
+      const uint32_t fmask = (kind == 32u) ? 0xFFFFFFFFu : ((1u << kind) - 1u);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], (uint32_t)kind);
-        store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], 32u - sft);
-        store_u32(rs, acc[c], (uint32_t)(l + 64 * c) * 4u, word_off);
-        acc[c] = __builtin_amdgcn_alignbit(f[c], acc[c], (uint32_t)kind);
+        const uint64_t wide = (uint64_t)(f[c] & fmask) << sft;
+        __hip_atomic_fetch_or(&codes[d * kDim + l + 64 * c], (uint32_t)wide, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_or(&codes[(d + 1) * kDim + l + 64 * c], (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
-    if ((ii & 3) == 3) QDR_FENCE();
+    QDR_FENCE();
   }
-  {
-    // tail word: the half's last field ends at bit `end`; if it does not fill
-    // its word, shift the pending bits down and zero-fill the top
-    const uint32_t mlast = meta[63];
-    const uint32_t end = (mlast & kRowOffMask) + (mlast >> kRowKindShift);
-    const uint32_t rem = end & 31u;
-    if (rem != 0u) {
-      const uint32_t word_off = half_off + (end >> 5) * (kDim * 4);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        store_u32(rs, acc[c] >> (32u - rem), (uint32_t)(l + 64 * c) * 4u, word_off);
-    }
-    // whole padding words of the half (granule count rounds up) stay zero
-    for (uint32_t dd = (end + 31u) >> 5; dd < (uint32_t)nwords; ++dd) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        store_u32(rs, 0u, (uint32_t)(l + 64 * c) * 4u, half_off + dd * (kDim * 4));
-    }
+  __builtin_amdgcn_wave_barrier();
+  // write this half's words back (the padding bits are the cleared zeros)
+  for (uint32_t off = (uint32_t)l * 16u; off < half_bytes; off += 1024u) {
+    const uint4 t = *reinterpret_cast<const uint4 *>(codes8 + off);
+    store_granule(rs, t, off, half_off);
   }
 
   // ---------------- column factor
@@ -954,13 +953,12 @@ k_rows(const LaunchArgs P) {
       if (w == 1) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          // wave 1's own chain started from zero; redo it from wave 0's sums
+          // wave 1's own sums started from zero; redo them from wave 0's
           float nn = sh.d[l + 64 * c], dd = sh.y[l + 64 * c];
 #pragma unroll
           for (int ii = 0; ii < 64; ++ii) {
-            const int kind = (int)(meta[ii] >> kRowKindShift);
-            if (kind <= 8) {
-              const float qm = sh.qm[64 + ii];
+            const float qm = sh.qm[64 + ii];
+            if (qm > 0.0f) {
               const float t = __builtin_fmaf(S[c][ii], ec[c] * qm, kMagic);
               const float zeta = (t - kMagic) * rn_div(1.0f, qm);
               const float pz = sh.m[64 + ii] * zeta;
@@ -972,8 +970,6 @@ k_rows(const LaunchArgs P) {
         }
       }
     }
-  } else if (SCALE == 0 && FIT) {
-    __syncthreads();   // keep the barrier count uniform across heads of one launch
   }
 
   // ---------------- readout
@@ -983,6 +979,7 @@ k_rows(const LaunchArgs P) {
     orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
     orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
   }
+#undef ROW_META
 }
 
 // --------------------------------------------------------------------------

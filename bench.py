@@ -48,12 +48,11 @@ def measured_traffic(cid: int):
     """HBM bytes per step from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     runs (scaled by a plain-copy calibration), or None when the kernel source
     has changed since those counters were taken."""
-    import hashlib
+    from quantized_delta_rule_decode_amd.build import device_source_hash
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "quantized_delta_rule_decode_amd", "csrc", "qdr_kernels.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = device_source_hash()
     except (OSError, ValueError):
         return None
     entry = rec.get(f"config{cid}")

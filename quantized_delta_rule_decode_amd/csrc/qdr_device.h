@@ -1,4 +1,5 @@
-// qdr_kernels.hip -- CDNA4 (gfx950) kernels of the quantized gated delta-rule
+#pragma once
+// qdr_device.h -- CDNA4 (gfx950) kernels of the quantized gated delta-rule
 // decode step.
 //
 // One workgroup of 128 threads (two wave64s) owns one (request, head) 128x128
@@ -983,7 +984,7 @@ k_rows(const LaunchArgs P) {
 }
 
 // --------------------------------------------------------------------------
-// dispatch
+// launch helpers (instantiated per storage kind in the qdr_head_*.hip units)
 // --------------------------------------------------------------------------
 namespace {
 
@@ -1010,77 +1011,17 @@ hipError_t launch_head_kind(const PoolConfig &cfg, const LaunchArgs &a, int n, h
   return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_heads(const PoolConfig &cfg, LaunchArgs a, int n, const int32_t *const *lists,
-                        const int32_t *counts, hipStream_t st) {
-  hipError_t e = hipSuccess;
-  for (int kidx = 0; kidx < 6 && e == hipSuccess; ++kidx) {
-    if (counts[kidx] == 0) continue;
-    a.head_list = lists[kidx];
-    a.n_list = counts[kidx];
-    switch (kidx) {
-      case 0: e = launch_head_kind<2, MODE>(cfg, a, n, st); break;
-      case 1: e = launch_head_kind<4, MODE>(cfg, a, n, st); break;
-      case 2: e = launch_head_kind<6, MODE>(cfg, a, n, st); break;
-      case 3: e = launch_head_kind<8, MODE>(cfg, a, n, st); break;
-      case 4: e = launch_head_kind<16, MODE>(cfg, a, n, st); break;
-      default: e = launch_head_kind<32, MODE>(cfg, a, n, st); break;
-    }
+// Every mode of the whole-head kernel for one storage kind.
+template <int BITS>
+hipError_t launch_head_modes(const PoolConfig &cfg, const LaunchArgs &a, int n, int mode, hipStream_t st) {
+  switch (mode) {
+    case MODE_STEP: return launch_head_kind<BITS, MODE_STEP>(cfg, a, n, st);
+    case MODE_PACK: return launch_head_kind<BITS, MODE_PACK>(cfg, a, n, st);
+    case MODE_UNPACK: return launch_head_kind<BITS, MODE_UNPACK>(cfg, a, n, st);
+    default: return launch_head_kind<BITS, MODE_RESET>(cfg, a, n, st);
   }
-  return e;
 }
 
 }  // namespace
-
-template <int MODE>
-hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const int32_t *list, int count,
-                       hipStream_t st) {
-  a.head_list = list;
-  a.n_list = count;
-  a.half_words = cfg.max_words;
-  const dim3 grid((unsigned)((int64_t)n * count)), block(128);
-  if (grid.x == 0) return hipSuccess;
-  const size_t lds = (size_t)2 * (cfg.max_words + 1) * kDim * sizeof(uint32_t);
-  const bool dual = cfg.scale_mode == 0, fit = cfg.fit_iters > 0, diag = cfg.gate == 1;
-  if (lds > 65536) {   // pools with FP32 rows: allow the larger dynamic LDS
-    const void *fns[6] = {(const void *)k_rows<MODE, 1, 1, 0>, (const void *)k_rows<MODE, 0, 1, 0>,
-                          (const void *)k_rows<MODE, 1, 0, 1>, (const void *)k_rows<MODE, 0, 0, 1>,
-                          (const void *)k_rows<MODE, 1, 0, 0>, (const void *)k_rows<MODE, 0, 0, 0>};
-    for (const void *f : fns) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-  }
-  if (!dual) {
-    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 1, 0>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((k_rows<MODE, 0, 1, 0>), grid, block, lds, st, a);
-  } else if (fit) {
-    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 1>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 1>), grid, block, lds, st, a);
-  } else {
-    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 0>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 0>), grid, block, lds, st, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const int32_t *const *kind_lists,
-                      const int32_t *kind_counts, int mode, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  if (cfg.unit != 0) {
-    switch (mode) {
-      case MODE_STEP: return launch_rows<MODE_STEP>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
-      case MODE_PACK: return launch_rows<MODE_PACK>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
-      case MODE_UNPACK: return launch_rows<MODE_UNPACK>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
-      default: return launch_rows<MODE_RESET>(cfg, args, n, kind_lists[0], kind_counts[0], stream);
-    }
-  }
-  switch (mode) {
-    case MODE_STEP: return launch_heads<MODE_STEP>(cfg, args, n, kind_lists, kind_counts, stream);
-    case MODE_PACK: return launch_heads<MODE_PACK>(cfg, args, n, kind_lists, kind_counts, stream);
-    case MODE_UNPACK: return launch_heads<MODE_UNPACK>(cfg, args, n, kind_lists, kind_counts, stream);
-    default: return launch_heads<MODE_RESET>(cfg, args, n, kind_lists, kind_counts, stream);
-  }
-}
 
 }  // namespace qdr

@@ -53,6 +53,18 @@ struct PoolConfig {
   int max_words;              // row units: largest words-per-column of any half
 };
 
+// Whole-head launches of one storage kind (args.head_list / n_list name the
+// heads of that kind), defined in qdr_head_<kind>.hip.
+hipError_t launch_head_b2(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
+hipError_t launch_head_b4(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
+hipError_t launch_head_b6(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
+hipError_t launch_head_b8(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
+hipError_t launch_head_b16(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
+hipError_t launch_head_b32(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
+// Row-unit launch (qdr_rows.hip) over the heads in list[0..count).
+hipError_t launch_rows_mode(const PoolConfig &, const LaunchArgs &, int n, const int32_t *list, int count,
+                            int mode, hipStream_t);
+
 // Launch every kernel of one mode over `n` requests / dense entries.
 // Returns hipSuccess or the first launch error.
 hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n,

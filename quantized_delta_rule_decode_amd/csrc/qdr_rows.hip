@@ -1,0 +1,53 @@
+// qdr_rows.hip -- row-unit kernels (per-key-row storage kinds) and their launch.
+#include "qdr_device.h"
+
+namespace qdr {
+
+namespace {
+
+template <int MODE>
+hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const int32_t *list, int count,
+                       hipStream_t st) {
+  a.head_list = list;
+  a.n_list = count;
+  a.half_words = cfg.max_words;
+  const dim3 grid((unsigned)((int64_t)n * count)), block(128);
+  if (grid.x == 0) return hipSuccess;
+  const size_t lds = (size_t)2 * (cfg.max_words + 1) * kDim * sizeof(uint32_t);
+  const bool dual = cfg.scale_mode == 0, fit = cfg.fit_iters > 0, diag = cfg.gate == 1;
+  if (lds > 65536) {   // pools with FP32 rows: allow the larger dynamic LDS
+    const void *fns[6] = {(const void *)k_rows<MODE, 1, 1, 0>, (const void *)k_rows<MODE, 0, 1, 0>,
+                          (const void *)k_rows<MODE, 1, 0, 1>, (const void *)k_rows<MODE, 0, 0, 1>,
+                          (const void *)k_rows<MODE, 1, 0, 0>, (const void *)k_rows<MODE, 0, 0, 0>};
+    for (const void *f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (!dual) {
+    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 1, 0>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((k_rows<MODE, 0, 1, 0>), grid, block, lds, st, a);
+  } else if (fit) {
+    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 1>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 1>), grid, block, lds, st, a);
+  } else {
+    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 0>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 0>), grid, block, lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+
+}  // namespace
+
+hipError_t launch_rows_mode(const PoolConfig &cfg, const LaunchArgs &a, int n, const int32_t *list, int count,
+                            int mode, hipStream_t st) {
+  switch (mode) {
+    case MODE_STEP: return launch_rows<MODE_STEP>(cfg, a, n, list, count, st);
+    case MODE_PACK: return launch_rows<MODE_PACK>(cfg, a, n, list, count, st);
+    case MODE_UNPACK: return launch_rows<MODE_UNPACK>(cfg, a, n, list, count, st);
+    default: return launch_rows<MODE_RESET>(cfg, a, n, list, count, st);
+  }
+}
+
+}  // namespace qdr

@@ -98,6 +98,33 @@ __device__ __forceinline__ uint32_t field_bits(const uint32_t *w, int ii) {
   return __builtin_amdgcn_alignbit(w[d + 1], w[d], s);
 }
 
+// n/16 for the 4-bit two's complement integer n in the low nibble of byte
+// SEL of w: v_cvt_off_f32_i4 (exact: n/16 has at most 4 significant bits)
+// reading its operand through an SDWA byte select.
+template <int SEL>
+__device__ __forceinline__ float nibble_over16(uint32_t w) {
+  float r;
+  if (SEL == 0) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if (SEL == 1) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if (SEL == 2) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+
+// INT4 field ii of a column-half stream as z/16 (nibble 2k of a word is the
+// low nibble of byte k, nibble 2k+1 the low nibble of byte k after a 4-bit
+// shift of the whole word).
+__device__ __forceinline__ float int4_field_over16(const uint32_t *w, int ii) {
+  const int d = ii >> 3, nib = ii & 7;
+  const uint32_t x = (nib & 1) ? (w[d] >> 4) : w[d];
+  switch (nib >> 1) {
+    case 0: return nibble_over16<0>(x);
+    case 1: return nibble_over16<1>(x);
+    case 2: return nibble_over16<2>(x);
+    default: return nibble_over16<3>(x);
+  }
+}
+
 template <int BITS>
 __device__ __forceinline__ float field_int_as_float(const uint32_t *w, int ii) {
   const int p = ii * BITS, d = p >> 5, s = p & 31;
@@ -124,7 +151,10 @@ __device__ __forceinline__ void put_field(uint32_t *out, uint32_t &acc, uint32_t
   } else {
     acc = __builtin_amdgcn_alignbit(f, acc, 32 - s);
     out[d] = acc;
-    acc = __builtin_amdgcn_alignbit(f, acc, BITS);
+    // the next word starts from f alone: whatever lies below f in the
+    // window is shifted out before that word is complete, so the word does
+    // not depend on this one (shorter dependency chains)
+    acc = __builtin_amdgcn_alignbit(f, 0u, BITS);
   }
 }
 
@@ -222,7 +252,9 @@ __device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red
 
 // Restore this wave's 64 rows of both lane columns into S (gate included).
 // CHAIN also runs acc_c = fma(x_i, S'_ic, acc_c) over those rows in order.
-template <int BITS, bool CHAIN>
+// OFF4 (INT4 only): the codes are converted as z/16 and gsh holds 16 g_i, so
+// z' * (16 g) is the same real number as z * g and rounds identically.
+template <int BITS, bool CHAIN, bool OFF4 = false>
 __device__ __forceinline__ void restore_rows(float (&S)[2][64], float (&acc)[2],
                                              const uint32_t (&wd)[2][Kind<BITS>::NW],
                                              const float (&colc)[2], const float *gsh,
@@ -241,7 +273,7 @@ __device__ __forceinline__ void restore_rows(float (&S)[2][64], float (&acc)[2],
       for (int c = 0; c < 2; ++c) {
         float sp;
         if (Kind<BITS>::is_int) {
-          const float zf = field_int_as_float<BITS>(wd[c], ii);
+          const float zf = OFF4 ? int4_field_over16(wd[c], ii) : field_int_as_float<BITS>(wd[c], ii);
           sp = (zf * gg[e]) * colc[c];
         } else if (BITS == 16) {
           sp = gg[e] * __half2float(__ushort_as_half((unsigned short)(field_bits<16>(wd[c], ii) & 0xFFFFu)));
@@ -271,10 +303,26 @@ __device__ __forceinline__ void chain_rows(const float (&S)[2][64], float (&acc)
   }
 }
 
+// DPP row move of x (dpp_ctrl CTRL, all rows and banks enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the wave's 64 lanes, returned to every lane (used for the readout
+// only, so the summation order is free): DPP butterflies inside each 16-lane
+// row (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror), then the four row sums from lanes 0, 16, 32 and 48.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 struct Shared {
@@ -311,22 +359,24 @@ struct Occupancy {
   static constexpr int waves = (BITS <= 8 && FIT == 0 && SCALE == 0) ? 3 : 2;
 };
 
+// The work of one (request b, head h) of kind BITS; sh is the workgroup's
+// LDS block.
 template <int BITS, int MODE, int GATE, int SCALE, int FIT>
-__global__ void __launch_bounds__(128)
-__attribute__((amdgpu_waves_per_eu(Occupancy<BITS, MODE, SCALE, FIT>::waves)))
-k_head(const LaunchArgs P) {
+__device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const int b, const int h,
+                                          const uint64_t head_off, const uint32_t code_bytes) {
   using K = Kind<BITS>;
   constexpr bool INT = K::is_int;
   constexpr float QMAX = (float)K::qmax_i;
-  __shared__ Shared sh;
+  // INT4 codes convert as z/16 (one SDWA instruction each); the 16 moves into
+  // the row factor.  Dual-axis row factors are at most sqrt(FLT_MAX / 2^-40),
+  // so 16 g_i stays finite; the row-absmax baseline keeps the plain path.
+  constexpr bool OFF4 = (BITS == 4) && (SCALE == 0);
+  constexpr float GSCALE = OFF4 ? 16.0f : 1.0f;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int row = 64 * w + l;
-  const int item = blockIdx.x;
-  const int b = item / P.n_list;
-  const int h = P.head_list[item - b * P.n_list];
   const size_t bh = (size_t)b * P.H + h;
   const int slot = P.slots[b];
 
@@ -342,8 +392,7 @@ k_head(const LaunchArgs P) {
     }
     return;
   }
-  uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + P.heads[h].off;
-  const uint32_t code_bytes = P.heads[h].code_bytes;
+  uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + head_off;
   const uint32_t blk_bytes = code_bytes + (INT ? (SCALE == 0 ? 2u : 1u) * kDim * 4u : 0u);
   const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(blk, 0, (int)blk_bytes, kRsrcWord3);
   const uint32_t half_off = (uint32_t)w * K::NG * (kDim * 16);   // this wave's first granule row
@@ -374,7 +423,7 @@ k_head(const LaunchArgs P) {
   if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
     if (INT) {
       const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
-      sh.g[row] = a_row * rn_div(r_row, QMAX);
+      sh.g[row] = (a_row * rn_div(r_row, QMAX)) * GSCALE;
       if (SCALE == 0) {
         colc[0] = load_f32(rs, (uint32_t)l * 4u, c_off);
         colc[1] = load_f32(rs, (uint32_t)l * 4u + 256u, c_off);
@@ -402,9 +451,9 @@ k_head(const LaunchArgs P) {
   // hand-off, wave 1 the other way round.
   float acc1[2] = {0.0f, 0.0f};
   if (MODE == MODE_STEP)
-    restore_rows<BITS, true>(S, acc1, wd, colc, sh.g, (w == 0) ? sh.k : sh.q, 64 * w);
+    restore_rows<BITS, true, OFF4>(S, acc1, wd, colc, sh.g, (w == 0) ? sh.k : sh.q, 64 * w);
   else if (MODE == MODE_UNPACK)
-    restore_rows<BITS, false>(S, acc1, wd, colc, sh.g, sh.g, 64 * w);
+    restore_rows<BITS, false, OFF4>(S, acc1, wd, colc, sh.g, sh.g, 64 * w);
 
   if (MODE == MODE_UNPACK) {
     float *dst = P.S_out + bh * kDim * kDim;
@@ -485,7 +534,10 @@ k_head(const LaunchArgs P) {
     __builtin_amdgcn_wave_barrier();
 
     // Y = S / r (in place) and the column maximum
-    float cm[2] = {0.0f, 0.0f};
+    // (two partial maxima per column, rows 4s+{0,1} and 4s+{2,3}: the
+    // maximum is exact in any order, and four independent chains keep the
+    // dependent v_max3 latency off the critical path)
+    float cm[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 r4 = lds4(&sh.ir[64 * w + 4 * i4]);
@@ -496,15 +548,15 @@ k_head(const LaunchArgs P) {
         for (int c = 0; c < 2; ++c) {
           const float y = S[c][4 * i4 + e] * rr[e];
           S[c][4 * i4 + e] = y;
-          cm[c] = fmaxf(cm[c], fabsf(y));
+          cm[c][e >> 1] = fmaxf(cm[c][e >> 1], fabsf(y));
         }
       }
       QDR_FENCE();
     }
     float c0[2] = {1.0f, 1.0f};
     if (SCALE == 0) {
-      sh.cmax[w][l] = cm[0];
-      sh.cmax[w][l + 64] = cm[1];
+      sh.cmax[w][l] = fmaxf(cm[0][0], cm[0][1]);
+      sh.cmax[w][l + 64] = fmaxf(cm[1][0], cm[1][1]);
     }
     if (MODE == MODE_STEP && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
     __syncthreads();
@@ -519,13 +571,12 @@ k_head(const LaunchArgs P) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) wq[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) * QMAX : QMAX;
 
-    // codes: pack and store one column at a time
+    // codes: both columns at once (two independent packing chains), then store
     float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
     constexpr float INVQ = INT ? 1.0f / (QMAX > 0.0f ? QMAX : 1.0f) : 0.0f;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t ow[K::NW];
-      uint32_t acc = 0;
+    {
+      uint32_t ow[2][K::NW];
+      uint32_t acc[2] = {0u, 0u};
 #pragma unroll
       for (int i4 = 0; i4 < 16; ++i4) {
         float mm[4] = {0, 0, 0, 0};
@@ -533,21 +584,37 @@ k_head(const LaunchArgs P) {
           const float4 m4 = lds4(&sh.m[64 * w + 4 * i4]);
           mm[0] = m4.x; mm[1] = m4.y; mm[2] = m4.z; mm[3] = m4.w;
         }
+        uint32_t tb[2][4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ii = 4 * i4 + e;
-          const float t = __builtin_fmaf(S[c][ii], wq[c], kMagic);
-          put_field<BITS>(ow, acc, __float_as_uint(t), ii);
-          if (FIT) {
-            const float zeta = (t - kMagic) * INVQ;
-            const float pz = mm[e] * zeta;
-            nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
-            dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float t = __builtin_fmaf(S[c][ii], wq[c], kMagic);
+            tb[c][e] = __float_as_uint(t);
+            if (BITS != 8) put_field<BITS>(ow[c], acc[c], __float_as_uint(t), ii);
+            if (FIT) {
+              const float zeta = (t - kMagic) * INVQ;
+              const float pz = mm[e] * zeta;
+              nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
+              dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
+            }
+          }
+        }
+        if (BITS == 8) {
+          // the low byte of each t is its two's complement code: gather the
+          // four bytes of rows 4*i4 .. 4*i4+3 with three byte permutes
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t lo = __builtin_amdgcn_perm(tb[c][1], tb[c][0], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(tb[c][3], tb[c][2], 0x0c0c0400u);
+            ow[c][i4] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
           }
         }
         QDR_FENCE();
       }
-      store_column<BITS>(rs, ow, (uint32_t)(l + 64 * c) * 16u, half_off);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) store_column<BITS>(rs, ow[c], (uint32_t)(l + 64 * c) * 16u, half_off);
     }
     // column factor
     if (SCALE == 0) {
@@ -612,6 +679,24 @@ k_head(const LaunchArgs P) {
   }
 }
 
+// One storage kind per launch: block = (request, entry of head_list).
+template <int BITS, int MODE, int GATE, int SCALE, int FIT>
+__global__ void __launch_bounds__(128)
+__attribute__((amdgpu_waves_per_eu(Occupancy<BITS, MODE, SCALE, FIT>::waves)))
+k_head(const LaunchArgs P) {
+  __shared__ Shared sh;
+  const int item = blockIdx.x;
+  const int b = item / P.n_list;
+  const ListEntry &e = P.head_list[item - b * P.n_list];
+  // v_readfirstlane is convergent, so these reads stay ahead of the padding /
+  // bad-slot branch (which stores): the entry is then read by one scalar load
+  // before anything is written, not by a vector load after the branch.
+  const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(e.info.off >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)e.info.off);
+  const uint32_t code_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)e.info.code_bytes);
+  head_body<BITS, MODE, GATE, SCALE, FIT>(P, sh, b, e.h, off, code_bytes);
+}
+
 // --------------------------------------------------------------------------
 // Row-unit kernel: each key row has its own kind (per-key-channel allocation
 // of the KDA variant, review "STEPQuant: When and Where Errors Matter in
@@ -641,7 +726,22 @@ k_rows(const LaunchArgs P) {
   const int row = 64 * w + l;
   const int item = blockIdx.x;
   const int b = item / P.n_list;
-  const int h = P.head_list[item - b * P.n_list];
+  const ListEntry &ent = P.head_list[item - b * P.n_list];
+  const int h = ent.h;
+  // read the whole entry ahead of the bad-slot branch (see k_head)
+  HeadInfo hi;
+  {
+    const uint32_t *ew = reinterpret_cast<const uint32_t *>(&ent.info);
+    uint32_t wv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wv[t] = (uint32_t)__builtin_amdgcn_readfirstlane((int)ew[t]);
+    hi.off = ((uint64_t)wv[1] << 32) | wv[0];
+    hi.code_bytes = wv[2];
+    hi.words0 = (uint8_t)wv[3];
+    hi.words1 = (uint8_t)(wv[3] >> 8);
+    hi.kind = (uint8_t)(wv[3] >> 16);
+    hi.has_scales = (uint8_t)(wv[3] >> 24);
+  }
   const size_t bh = (size_t)b * P.H + h;
   const int slot = P.slots[b];
 
@@ -658,7 +758,6 @@ k_rows(const LaunchArgs P) {
     }
     return;
   }
-  const HeadInfo hi = P.heads[h];
   const int has_int = hi.has_scales;
   uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + hi.off;
   const uint32_t code_bytes = hi.code_bytes;

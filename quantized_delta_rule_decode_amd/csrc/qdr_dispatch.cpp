@@ -4,7 +4,7 @@
 
 namespace qdr {
 
-hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const int32_t *const *kind_lists,
+hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const ListEntry *const *kind_lists,
                       const int32_t *kind_counts, int mode, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   if (cfg.unit != 0) return launch_rows_mode(cfg, args, n, kind_lists[0], kind_counts[0], mode, stream);

@@ -23,6 +23,15 @@ struct HeadInfo {
   uint8_t has_scales;   // 1 when the block stores r (and c)
 };
 
+// One entry of a launch's head list (32 bytes, read with one scalar load):
+// the head's table row and its index.
+struct ListEntry {
+  HeadInfo info;
+  int32_t h;
+  int32_t pad[3];
+};
+static_assert(sizeof(HeadInfo) == 16 && sizeof(ListEntry) == 32, "device table layout");
+
 // Row units: per (head, row) word = bit offset of the row inside its half of
 // the column stream (bits 0..15) | kind (bits 16..23).
 constexpr uint32_t kRowOffMask = 0xFFFFu;
@@ -34,8 +43,7 @@ struct LaunchArgs {
   uint64_t slot_stride;
   int32_t num_slots;
   int32_t H;
-  const HeadInfo *heads;
-  const int32_t *head_list;   // heads handled by this launch
+  const ListEntry *head_list;   // heads handled by this launch
   int32_t n_list;
   const uint32_t *row_meta;   // [H*128] (row units), see kRowOffMask
   int32_t half_words;         // row units: LDS words reserved per column and half
@@ -62,13 +70,17 @@ hipError_t launch_head_b8(const PoolConfig &, const LaunchArgs &, int n, int mod
 hipError_t launch_head_b16(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 hipError_t launch_head_b32(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 // Row-unit launch (qdr_rows.hip) over the heads in list[0..count).
-hipError_t launch_rows_mode(const PoolConfig &, const LaunchArgs &, int n, const int32_t *list, int count,
+hipError_t launch_rows_mode(const PoolConfig &, const LaunchArgs &, int n, const ListEntry *list, int count,
                             int mode, hipStream_t);
+
+// Number of head lists a pool keeps: one per kind (INT2, INT4, INT6, INT8,
+// FP16, FP32) for whole-head units; row-unit pools keep all heads in list 0.
+constexpr int kNumLists = 6;
 
 // Launch every kernel of one mode over `n` requests / dense entries.
 // Returns hipSuccess or the first launch error.
 hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n,
-                      const int32_t *const *kind_lists, const int32_t *kind_counts,
+                      const ListEntry *const *kind_lists, const int32_t *kind_counts,
                       int mode, hipStream_t stream);
 
 }  // namespace qdr

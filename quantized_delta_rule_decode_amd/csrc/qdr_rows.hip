@@ -6,7 +6,7 @@ namespace qdr {
 namespace {
 
 template <int MODE>
-hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const int32_t *list, int count,
+hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const ListEntry *list, int count,
                        hipStream_t st) {
   a.head_list = list;
   a.n_list = count;
@@ -40,7 +40,7 @@ hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const int32_t
 
 }  // namespace
 
-hipError_t launch_rows_mode(const PoolConfig &cfg, const LaunchArgs &a, int n, const int32_t *list, int count,
+hipError_t launch_rows_mode(const PoolConfig &cfg, const LaunchArgs &a, int n, const ListEntry *list, int count,
                             int mode, hipStream_t st) {
   switch (mode) {
     case MODE_STEP: return launch_rows<MODE_STEP>(cfg, a, n, list, count, st);

@@ -159,12 +159,11 @@ struct qdr_pool {
   int device = 0;
   uint8_t *base = nullptr;
   bool owns_base = false;
-  qdr::HeadInfo *d_heads = nullptr;
   uint32_t *d_row_meta = nullptr;
   float *d_omega = nullptr;
   uint32_t *d_err = nullptr;
-  int32_t *d_lists[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  int32_t list_count[6] = {0, 0, 0, 0, 0, 0};
+  qdr::ListEntry *d_lists[qdr::kNumLists] = {};
+  int32_t list_count[qdr::kNumLists] = {};
 };
 
 namespace {
@@ -181,7 +180,6 @@ hipError_t upload(T **dst, const T *src, size_t n) {
 void free_pool(qdr_pool *p) {
   if (!p) return;
   if (p->owns_base && p->base) (void)hipFree(p->base);
-  (void)hipFree(p->d_heads);
   (void)hipFree(p->d_row_meta);
   (void)hipFree(p->d_omega);
   (void)hipFree(p->d_err);
@@ -195,7 +193,6 @@ qdr::LaunchArgs base_args(const qdr_pool *p) {
   a.slot_stride = p->L.slot_stride;
   a.num_slots = p->desc.num_slots;
   a.H = p->desc.num_heads;
-  a.heads = p->d_heads;
   a.row_meta = p->d_row_meta;
   a.omega = p->d_omega;
   a.err = p->d_err;
@@ -221,8 +218,8 @@ qdr_status check_slots_host(const qdr_pool *p, const int32_t *slots, int32_t n, 
 }
 
 qdr_status dispatch(qdr_pool *p, qdr::LaunchArgs a, int n, int mode, hipStream_t st) {
-  const int32_t *lists[6];
-  for (int i = 0; i < 6; ++i) lists[i] = p->d_lists[i];
+  const qdr::ListEntry *lists[qdr::kNumLists];
+  for (int i = 0; i < qdr::kNumLists; ++i) lists[i] = p->d_lists[i];
   hipError_t e = qdr::launch_all(p->cfg, a, n, lists, p->list_count, mode, st);
   if (e == hipErrorNotSupported) return fail(QDR_E_UNSUPPORTED, "this pool configuration has no kernel");
   if (e != hipSuccess) return fail(QDR_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
@@ -280,7 +277,7 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
     p->owns_base = true;
   }
   std::vector<qdr::HeadInfo> hi(desc->num_heads);
-  std::vector<std::vector<int32_t>> lists(6);
+  std::vector<std::vector<qdr::ListEntry>> lists(qdr::kNumLists);
   for (int h = 0; h < desc->num_heads; ++h) {
     hi[h].off = p->L.head_off[h];
     hi[h].code_bytes = p->L.code_bytes[h];
@@ -288,16 +285,18 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
     hi[h].words1 = p->L.words1[h];
     hi[h].kind = desc->unit == QDR_UNIT_HEAD ? p->kinds[h] : 0;
     hi[h].has_scales = p->L.has_scales[h];
-    if (desc->unit == QDR_UNIT_HEAD) lists[kind_index(p->kinds[h])].push_back(h);
-    else lists[0].push_back(h);
+    qdr::ListEntry le{};
+    le.info = hi[h];
+    le.h = h;
+    if (desc->unit == QDR_UNIT_HEAD) lists[kind_index(p->kinds[h])].push_back(le);
+    else lists[0].push_back(le);
   }
   hipError_t e = hipMemset(p->base, 0, total);
-  if (e == hipSuccess) e = upload(&p->d_heads, hi.data(), hi.size());
   if (e == hipSuccess) e = upload(&p->d_omega, p->omega.data(), p->omega.size());
   if (e == hipSuccess && desc->unit == QDR_UNIT_ROW) {
     e = upload(&p->d_row_meta, p->L.row_meta.data(), p->L.row_meta.size());
   }
-  for (int i = 0; i < 6 && e == hipSuccess; ++i) {
+  for (int i = 0; i < qdr::kNumLists && e == hipSuccess; ++i) {
     p->list_count[i] = (int32_t)lists[i].size();
     e = upload(&p->d_lists[i], lists[i].data(), lists[i].size());
   }

@@ -166,8 +166,9 @@ __device__ __forceinline__ void put_field(uint32_t *out, uint32_t &acc, uint32_t
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) dword access on CDNA
 
+// Code granules are read once per step: nontemporal (nt) loads.
 __device__ __forceinline__ uint4 load_granule(rsrc_t rs, uint32_t voff, uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 2);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -697,6 +698,36 @@ k_head(const LaunchArgs P) {
   head_body<BITS, MODE, GATE, SCALE, FIT>(P, sh, b, e.h, off, code_bytes);
 }
 
+// Every integer kind in one launch.  head_list interleaves the integer heads
+// of the different widths in proportion to their counts, so each compute
+// unit runs a mix of them at any time: the narrow widths are bound by vector
+// ALU work and the wide ones by HBM traffic, and mixed they overlap instead
+// of running as separate back-to-back launches.  The kind is read per block
+// (uniform across the workgroup), so the branch below is scalar.
+template <int MODE, int GATE, int SCALE, int FIT>
+__global__ void __launch_bounds__(128)
+__attribute__((amdgpu_waves_per_eu(Occupancy<8, MODE, SCALE, FIT>::waves)))
+k_head_int(const LaunchArgs P) {
+  __shared__ Shared sh;
+  const int item = blockIdx.x;
+  const int b = item / P.n_list;
+  const ListEntry &e = P.head_list[item - b * P.n_list];
+  // the entry's words through v_readfirstlane (scalar loads ahead of the
+  // padding branch, see k_head)
+  const uint32_t *ew = reinterpret_cast<const uint32_t *>(&e);
+  uint32_t wv[5];
+#pragma unroll
+  for (int t = 0; t < 5; ++t) wv[t] = (uint32_t)__builtin_amdgcn_readfirstlane((int)ew[t]);
+  const uint64_t off = ((uint64_t)wv[1] << 32) | wv[0];
+  const uint32_t code_bytes = wv[2];
+  const int kind = (int)((wv[3] >> 16) & 0xFFu);
+  const int h = (int)wv[4];
+  if (kind == 6) head_body<6, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
+  else if (kind == 8) head_body<8, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
+  else if (kind == 4) head_body<4, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
+  else head_body<2, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
+}
+
 // --------------------------------------------------------------------------
 // Row-unit kernel: each key row has its own kind (per-key-channel allocation
 // of the KDA variant, review "STEPQuant: When and Where Errors Matter in
@@ -1106,6 +1137,26 @@ hipError_t launch_head_kind(const PoolConfig &cfg, const LaunchArgs &a, int n, h
   } else {
     if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 0>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 0, 0>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_head_int_mode(const PoolConfig &cfg, const LaunchArgs &a, int n, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)n * a.n_list)), block(128);
+  if (grid.x == 0) return hipSuccess;
+  const bool dual = cfg.scale_mode == 0;
+  const bool fit = cfg.fit_iters > 0;
+  const bool diag = cfg.gate == 1;
+  if (!dual) {
+    if (diag) hipLaunchKernelGGL((k_head_int<MODE, 1, 1, 0>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_head_int<MODE, 0, 1, 0>), grid, block, 0, st, a);
+  } else if (fit) {
+    if (diag) hipLaunchKernelGGL((k_head_int<MODE, 1, 0, 1>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_head_int<MODE, 0, 0, 1>), grid, block, 0, st, a);
+  } else {
+    if (diag) hipLaunchKernelGGL((k_head_int<MODE, 1, 0, 0>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_head_int<MODE, 0, 0, 0>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

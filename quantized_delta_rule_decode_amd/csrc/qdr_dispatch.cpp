@@ -1,5 +1,6 @@
 // qdr_dispatch.cpp -- picks the kernels of one mode: the row-unit kernel, or
-// one whole-head launch per storage kind present, back to back on the stream.
+// for whole-head pools one launch over every integer head (kinds mixed) and
+// one launch per float kind present, back to back on the stream.
 #include "qdr_internal.h"
 
 namespace qdr {
@@ -8,15 +9,26 @@ hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const ListE
                       const int32_t *kind_counts, int mode, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   if (cfg.unit != 0) return launch_rows_mode(cfg, args, n, kind_lists[0], kind_counts[0], mode, stream);
-  typedef hipError_t (*head_fn)(const PoolConfig &, const LaunchArgs &, int, int, hipStream_t);
-  static const head_fn fns[6] = {launch_head_b2, launch_head_b4, launch_head_b6,
-                                 launch_head_b8, launch_head_b16, launch_head_b32};
   hipError_t e = hipSuccess;
-  for (int kidx = 0; kidx < 6 && e == hipSuccess; ++kidx) {
-    if (kind_counts[kidx] == 0) continue;
-    args.head_list = kind_lists[kidx];
-    args.n_list = kind_counts[kidx];
-    e = fns[kidx](cfg, args, n, mode, stream);
+  if (kind_counts[kListIntMix] > 0) {
+    args.head_list = kind_lists[kListIntMix];
+    args.n_list = kind_counts[kListIntMix];
+    switch (mode) {
+      case MODE_STEP: e = launch_head_int_step(cfg, args, n, stream); break;
+      case MODE_PACK: e = launch_head_int_pack(cfg, args, n, stream); break;
+      case MODE_UNPACK: e = launch_head_int_unpack(cfg, args, n, stream); break;
+      default: e = launch_head_int_reset(cfg, args, n, stream); break;
+    }
+  }
+  if (e == hipSuccess && kind_counts[4] > 0) {
+    args.head_list = kind_lists[4];
+    args.n_list = kind_counts[4];
+    e = launch_head_b16(cfg, args, n, mode, stream);
+  }
+  if (e == hipSuccess && kind_counts[5] > 0) {
+    args.head_list = kind_lists[5];
+    args.n_list = kind_counts[5];
+    e = launch_head_b32(cfg, args, n, mode, stream);
   }
   return e;
 }

@@ -61,21 +61,25 @@ struct PoolConfig {
   int max_words;              // row units: largest words-per-column of any half
 };
 
-// Whole-head launches of one storage kind (args.head_list / n_list name the
-// heads of that kind), defined in qdr_head_<kind>.hip.
-hipError_t launch_head_b2(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
-hipError_t launch_head_b4(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
-hipError_t launch_head_b6(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
-hipError_t launch_head_b8(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
+// Whole-head launches.  Integer kinds share one launch per mode
+// (qdr_head_int_<mode>.hip) over the interleaved list of integer heads;
+// FP16 and FP32 heads get one launch each (qdr_head_fp16.hip,
+// qdr_head_fp32.hip).  args.head_list / n_list name the heads.
+hipError_t launch_head_int_step(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
+hipError_t launch_head_int_pack(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
+hipError_t launch_head_int_unpack(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
+hipError_t launch_head_int_reset(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_b16(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 hipError_t launch_head_b32(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 // Row-unit launch (qdr_rows.hip) over the heads in list[0..count).
 hipError_t launch_rows_mode(const PoolConfig &, const LaunchArgs &, int n, const ListEntry *list, int count,
                             int mode, hipStream_t);
 
-// Number of head lists a pool keeps: one per kind (INT2, INT4, INT6, INT8,
-// FP16, FP32) for whole-head units; row-unit pools keep all heads in list 0.
-constexpr int kNumLists = 6;
+// Number of head lists a pool keeps: per kind (INT2, INT4, INT6, INT8, FP16,
+// FP32) and, last, every integer head interleaved by kind (whole-head units;
+// row-unit pools keep all heads in list 0).
+constexpr int kNumLists = 7;
+constexpr int kListIntMix = 6;
 
 // Launch every kernel of one mode over `n` requests / dense entries.
 // Returns hipSuccess or the first launch error.

@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -177,6 +178,25 @@ hipError_t upload(T **dst, const T *src, size_t n) {
   return hipMemcpy(*dst, src, n * sizeof(T), hipMemcpyHostToDevice);
 }
 
+// Every integer head (lists 0..3, one per width), merged so that each width
+// is spread evenly over the list: entry r of a width with n heads sits at
+// position (r + 1/2) / n of the way through; ties keep width order.
+std::vector<qdr::ListEntry> interleave_int_heads(const std::vector<std::vector<qdr::ListEntry>> &lists) {
+  struct Key { double pos; int kind; qdr::ListEntry e; };
+  std::vector<Key> keys;
+  for (int k = 0; k < 4; ++k) {
+    const size_t n = lists[k].size();
+    for (size_t r = 0; r < n; ++r) keys.push_back({(r + 0.5) / (double)n, k, lists[k][r]});
+  }
+  std::stable_sort(keys.begin(), keys.end(), [](const Key &a, const Key &b) {
+    return a.pos < b.pos || (a.pos == b.pos && a.kind < b.kind);
+  });
+  std::vector<qdr::ListEntry> out;
+  out.reserve(keys.size());
+  for (const Key &k : keys) out.push_back(k.e);
+  return out;
+}
+
 void free_pool(qdr_pool *p) {
   if (!p) return;
   if (p->owns_base && p->base) (void)hipFree(p->base);
@@ -291,6 +311,7 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
     if (desc->unit == QDR_UNIT_HEAD) lists[kind_index(p->kinds[h])].push_back(le);
     else lists[0].push_back(le);
   }
+  if (desc->unit == QDR_UNIT_HEAD) lists[qdr::kListIntMix] = interleave_int_heads(lists);
   hipError_t e = hipMemset(p->base, 0, total);
   if (e == hipSuccess) e = upload(&p->d_omega, p->omega.data(), p->omega.size());
   if (e == hipSuccess && desc->unit == QDR_UNIT_ROW) {

@@ -77,6 +77,50 @@ def cpu_baseline(cfg, tables, requests: int, threads: int):
     return requests * cfg.H / dt, dt
 
 
+def time_on_stream(fn, reps: int, warmup: int = 1) -> float:
+    """Mean ms per call of fn() (device work on torch's current stream),
+    HIP events recorded on that stream around `reps` calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def fp32_comparator(cfg, f32_pool, inputs, o, reps: int = 4):
+    """The same decode step on an unquantised FP32 state pool of the same shape
+    (the warm-up pool): the packed/FP32 speedup is the analogue of the pages'
+    state-update speedup of the packed state over the FP32 state."""
+    import torch
+    B = cfg.B
+    ident = torch.arange(B, dtype=torch.int32, device=o.device)
+    ms = time_on_stream(lambda: f32_pool.qdr_decode_step(ident, *inputs, o), reps)
+    per_head = 2 * 128 * 128 * 4 + 3 * 128 * 4 + 4 + (4 if cfg.gate == 0 else 4 * 128) + 128 * 4
+    nbytes = per_head * B * cfg.H
+    return {"ms_per_step": ms, "value": B * cfg.H / (ms * 1e-3), "unit": "state-update steps/s",
+            "bytes_per_step": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "state": "fp32, 64 KiB per head, same kernel family (whole-head FP32 kind)"}
+
+
+def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
+    """HBM rate of a plain in-place streaming kernel on this GPU (torch add_ of
+    an fp32 buffer: each byte read once and written once), for scale."""
+    import torch
+    x = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    ms = time_on_stream(lambda: x.add_(1.0), reps)
+    del x
+    return {"kernel": "torch.Tensor.add_ (in place, fp32)", "bytes": 2 * nbytes,
+            "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +131,8 @@ def main():
                     help="FP32 delta-rule steps that build the warm state (default: the config's)")
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp32-comparator", action="store_true",
+                    help="skip timing the FP32-state pool of the warm-up")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -116,14 +162,17 @@ def main():
     pool = workload.make_pool(cfg, tables)
     slots = torch.from_numpy(tables["slots"]).to(dev)
     warm = cfg.warmup if args.fp32_warmup_steps is None else args.fp32_warmup_steps
+    q, k, v, beta, gate = workload.step_inputs(cfg, tables, 0, device=dev)
+    o = torch.empty((cfg.B, cfg.H, 128), dtype=torch.float32, device=dev)
+    fp32_cmp = None
     if warm > 0:
         f32 = workload.warm_start(cfg, tables, pool, slots, warm)
+        if not args.no_fp32_comparator:
+            fp32_cmp = fp32_comparator(cfg, f32, (q, k, v, beta, gate), o)
         f32.close()
         del f32
     else:
         pool.qdr_slot_reset(slots)
-    q, k, v, beta, gate = workload.step_inputs(cfg, tables, 0, device=dev)
-    o = torch.empty((cfg.B, cfg.H, 128), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -149,6 +198,7 @@ def main():
     achieved = nbytes / (gpu_ms * 1e-3) / 1e9
     value = head_steps / (gpu_ms * 1e-3)
 
+    stream = stream_reference()
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(os.cpu_count() or 1, 16)
@@ -177,9 +227,15 @@ def main():
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "unit_of_work": "one qdr_decode_step = one kernel launch per storage kind, back to back "
-                                     "on one stream; achieved = algorithmic bytes / step time",
-                     "traffic_over_algorithmic": None if traffic is None else traffic / nbytes},
+                     "unit_of_work": ("one qdr_decode_step: whole-head pools launch k_head_int over every "
+                                      "integer head (the dominant kernel) plus one launch per float kind, "
+                                      "back to back on one stream; row-unit pools launch k_rows once; "
+                                      "achieved = algorithmic bytes per step / step time"),
+                     "traffic_over_algorithmic": None if traffic is None else traffic / nbytes,
+                     "stream_reference": stream,
+                     "frac_of_stream_reference": achieved / stream["GBps"]},
+        "fp32_state_comparator": None if fp32_cmp is None else {
+            **fp32_cmp, "speedup_packed_over_fp32": fp32_cmp["ms_per_step"] / gpu_ms},
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "setup_s": setup_s,

@@ -125,6 +125,15 @@ __device__ __forceinline__ float int4_field_over16(const uint32_t *w, int ii) {
   }
 }
 
+// Sign-extended low `width` bits of x (v_bfe_i32 with a wave-uniform width
+// operand).  Written as a single instruction so that the result is known to
+// the compiler only as a signed 32-bit value.
+__device__ __forceinline__ int32_t sext_low(uint32_t x, uint32_t width) {
+  int32_t r;
+  asm("v_bfe_i32 %0, %1, 0, %2" : "=v"(r) : "v"(x), "s"(width));
+  return r;
+}
+
 template <int BITS>
 __device__ __forceinline__ float field_int_as_float(const uint32_t *w, int ii) {
   const int p = ii * BITS, d = p >> 5, s = p & 31;
@@ -235,15 +244,21 @@ __device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red
     if (s & 1) QDR_FENCE();
   }
   __builtin_amdgcn_wave_barrier();
-  float x[16];
+  // the first fold (i with i + 8) as the partials arrive, so at most eight
+  // of them are live next to the tile
+  float x[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 t = lds4(&red[lane][4 * i]);
-    x[4 * i + 0] = t.x; x[4 * i + 1] = t.y; x[4 * i + 2] = t.z; x[4 * i + 3] = t.w;
+  for (int i = 0; i < 2; ++i) {
+    const float4 t0 = lds4(&red[lane][4 * i]);
+    const float4 t1 = lds4(&red[lane][4 * i + 8]);
+    x[4 * i + 0] = MAX ? fmaxf(t0.x, t1.x) : t0.x + t1.x;
+    x[4 * i + 1] = MAX ? fmaxf(t0.y, t1.y) : t0.y + t1.y;
+    x[4 * i + 2] = MAX ? fmaxf(t0.z, t1.z) : t0.z + t1.z;
+    x[4 * i + 3] = MAX ? fmaxf(t0.w, t1.w) : t0.w + t1.w;
   }
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int half = 8; half >= 1; half >>= 1) {
+  for (int half = 4; half >= 1; half >>= 1) {
 #pragma unroll
     for (int i = 0; i < half; ++i) x[i] = MAX ? fmaxf(x[i], x[i + half]) : x[i] + x[i + half];
   }
@@ -326,7 +341,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (r0 + r1) + (r2 + r3);
 }
 
-struct Shared {
+struct SharedCore {
   float g[kDim];     // restore factor a_i * r_i / q_i (or a_i for float kinds)
   float k[kDim];
   float b[kDim];     // beta * k_i
@@ -340,7 +355,10 @@ struct Shared {
   float qm[kDim];    // row units: largest code of the row's grid (0 for float rows)
   float iq[kDim];    // row units: 1/qm (0 for float rows)
   float qb[2];       // each wave's part of sum_i q_i b_i
-  float red[2][64][20];
+};
+
+struct Shared : SharedCore {
+  float red[2][64][20];   // row-reduction transpose scratch, one block per wave
 };
 
 }  // namespace
@@ -728,28 +746,69 @@ k_head_int(const LaunchArgs P) {
   else head_body<2, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
 }
 
+typedef const __attribute__((address_space(4))) RowProg *const_rowprog_t;
+
+// entry i of a row table, copied field by field out of the constant space
+__device__ __forceinline__ RowProg row_op(const_rowprog_t p, int i) {
+  RowProg r;
+  r.xs = p[i].xs;
+  r.z = p[i].z;
+  return r;
+}
+
+// Append one field of `kind` bits (1..16) at stream bit `off` of a
+// column-half stream to the two column windows of a lane.  A window holds
+// the last 32 stream bits written, newest at the top: the funnel shift by the
+// width brings the field's low `kind` bits in from the top.  When the field
+// reaches or crosses the end of its word, that word -- the window shifted by
+// the bits that were missing -- is written to LDS (out: [word][column] of the
+// half).  Whatever is left below the field after a crossing is shifted out
+// before the next word completes.
+__device__ __forceinline__ void append_field(uint32_t *out, int l, uint32_t (&win)[2], uint32_t f0,
+                                             uint32_t f1, uint32_t off, uint32_t kind) {
+  const uint32_t sft = off & 31u;
+  if (sft + kind >= 32u) {
+    uint32_t *o = out + (off >> 5) * kDim + l;
+    o[0] = __builtin_amdgcn_alignbit(f0, win[0], 32u - sft);
+    o[64] = __builtin_amdgcn_alignbit(f1, win[1], 32u - sft);
+  }
+  win[0] = __builtin_amdgcn_alignbit(f0, win[0], kind);
+  win[1] = __builtin_amdgcn_alignbit(f1, win[1], kind);
+}
+
 // --------------------------------------------------------------------------
 // Row-unit kernel: each key row has its own kind (per-key-channel allocation
 // of the KDA variant, review "STEPQuant: When and Where Errors Matter in
 // Delta-Rule Recurrent State Quantization", Method).  Same thread mapping and
 // arithmetic as k_head.  Row widths are data, so:
-//   * each wave stages its half of the column streams in LDS and reads a
-//     row's field at a run-time bit offset (funnel shift of two words);
-//   * row metadata (bit offset | kind) is read back per row with v_readlane,
-//     so it is wave-uniform (SGPR) and every branch on it is scalar;
-//   * integer rows run straight-line code; the rare FP16/FP32 rows patch
-//     their values in a uniform branch;
-//   * repacking ORs each field into a zeroed LDS copy of the half
-//     (ds_or_b32 on the one or two words it touches), which is then stored
-//     with 16-byte coalesced writes: no per-row flush logic.
-// LDS reserves half_words + 1 words per column so the second word of a
-// field's funnel shift stays inside the wave's region.
+//   * each wave stages its half of the column streams in LDS; the per-row
+//     program (word offset, bit offset, width, completing shift) is read
+//     with scalar loads and used directly as instruction operands, so no
+//     per-row scalar arithmetic runs;
+//   * R1 restores every row as an integer row (a funnel shift of two words,
+//     then one sign-extending extract of the row's width), straight-line;
+//     rows stored as FP16/FP32 pivots are redone in uniform branches (R2)
+//     only when the half holds any;
+//   * repacking: every value becomes its code bits in place (P1), pivot rows
+//     take their stored bits from an LDS stash, then each row's field is
+//     appended to per-column register windows (P2); the word a field ends in
+//     is written to LDS at once (a later field of the same word overwrites
+//     it), and the half goes out with 16-byte stores.  Halves holding FP32
+//     rows append in uniform branches instead.
+// LDS: each wave's region holds the staged words of its half (one spare row
+// so the second word of a funnel shift stays in range); after the restore it
+// serves as the row reduction's scratch, the pivot stash and the output
+// image of the half.
 // --------------------------------------------------------------------------
 template <int MODE, int GATE, int SCALE, int FIT>
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(128)
+// two waves per SIMD: the row tables, the pivot bookkeeping and the LDS
+// addressing leave no room for the three-wave budget of 168 VGPRs (the
+// allocator spills there, which costs more than the third wave gains)
+__attribute__((amdgpu_waves_per_eu(2)))
 k_rows(const LaunchArgs P) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_codes[];   // 16-byte aligned: staged with ds_write_b128
-  __shared__ Shared sh;
+  __shared__ SharedCore sh;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -758,21 +817,18 @@ k_rows(const LaunchArgs P) {
   const int item = blockIdx.x;
   const int b = item / P.n_list;
   const ListEntry &ent = P.head_list[item - b * P.n_list];
-  const int h = ent.h;
   // read the whole entry ahead of the bad-slot branch (see k_head)
-  HeadInfo hi;
+  uint32_t ev[5];
   {
-    const uint32_t *ew = reinterpret_cast<const uint32_t *>(&ent.info);
-    uint32_t wv[4];
+    const uint32_t *ew = reinterpret_cast<const uint32_t *>(&ent);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wv[t] = (uint32_t)__builtin_amdgcn_readfirstlane((int)ew[t]);
-    hi.off = ((uint64_t)wv[1] << 32) | wv[0];
-    hi.code_bytes = wv[2];
-    hi.words0 = (uint8_t)wv[3];
-    hi.words1 = (uint8_t)(wv[3] >> 8);
-    hi.kind = (uint8_t)(wv[3] >> 16);
-    hi.has_scales = (uint8_t)(wv[3] >> 24);
+    for (int t = 0; t < 5; ++t) ev[t] = (uint32_t)__builtin_amdgcn_readfirstlane((int)ew[t]);
   }
+  const uint64_t blk_off = ((uint64_t)ev[1] << 32) | ev[0];
+  const uint32_t code_bytes = ev[2];
+  const int words0 = (int)(ev[3] & 0xFFu), words1 = (int)((ev[3] >> 8) & 0xFFu);
+  const int has_int = (int)(ev[3] >> 24);
+  const int h = (int)ev[4];
   const size_t bh = (size_t)b * P.H + h;
   const int slot = P.slots[b];
 
@@ -789,38 +845,40 @@ k_rows(const LaunchArgs P) {
     }
     return;
   }
-  const int has_int = hi.has_scales;
-  uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + hi.off;
-  const uint32_t code_bytes = hi.code_bytes;
+  uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + blk_off;
   const uint32_t blk_bytes = code_bytes + (has_int ? (SCALE == 0 ? 2u : 1u) * kDim * 4u : 0u);
   const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(blk, 0, (int)blk_bytes, kRsrcWord3);
-  const int nwords = (w == 0) ? hi.words0 : hi.words1;              // words per column, this half
-  const uint32_t half_off = (w == 0) ? 0u : (uint32_t)hi.words0 * (kDim * 4);
+  const int nwords = (w == 0) ? words0 : words1;                    // words per column, this half
+  const uint32_t half_off = (w == 0) ? 0u : (uint32_t)words0 * (kDim * 4);
   const uint32_t half_bytes = (uint32_t)nwords * (kDim * 4);
   const uint32_t r_off = code_bytes, c_off = code_bytes + kDim * 4;
-  uint32_t *codes = lds_codes + (size_t)w * (P.half_words + 1) * kDim;   // [word][column]
+  uint32_t *codes = lds_codes + (size_t)w * P.region_rows * kDim;   // [word][column]
   uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
-
-  // row metadata of this wave's 64 rows: lane l holds row 64w+l's word, and
-  // row ii's word is read back with v_readlane (an SGPR value)
-  const uint32_t meta_lane = P.row_meta[(size_t)h * kDim + 64 * w + l];
-#define ROW_META(ii) ((uint32_t)__builtin_amdgcn_readlane((int)meta_lane, (ii)))
+  const uint32_t lane_byte = (uint32_t)l * 4u;                       // column l of word 0
+  // this half's rows, read through the constant address space: the tables
+  // never change during a launch, so every read is a scalar load (batched
+  // by the compiler) even after the kernel has stored
+  const const_rowprog_t uprog = (const_rowprog_t)(P.row_unpack + (size_t)h * kDim + 64 * w);
+  const const_rowprog_t pprog = (const_rowprog_t)(P.row_pack + (size_t)h * kDim + 64 * w);
 
   float S[2][64];
   float colc[2] = {1.0f, 1.0f};
 
   // ---------------- stage this half's code words in LDS (1 KiB per wave instruction)
   if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
-    for (uint32_t off = (uint32_t)l * 16u; off < half_bytes; off += 1024u)
-      *reinterpret_cast<uint4 *>(codes8 + off) = load_granule(rs, off, half_off);
+    for (uint32_t boff = (uint32_t)l * 16u; boff < half_bytes; boff += 1024u)
+      *reinterpret_cast<uint4 *>(codes8 + boff) = load_granule(rs, boff, half_off);
     codes[nwords * kDim + l] = 0u;
     codes[nwords * kDim + 64 + l] = 0u;
   }
 
   // ---------------- per-row scalars of this lane's row
-  const int my_kind = (int)(meta_lane >> kRowKindShift);
+  const int my_kind = (int)uprog[l].z;
   const bool my_int = my_kind <= 8;
   const float my_q = my_int ? (float)((1 << (my_kind - 1)) - 1) : 0.0f;
+  // rows of this half stored as FP16/FP32 pivots, and as FP32 (bit ii = row 64w+ii)
+  const uint64_t pivots = __ballot(!my_int);
+  const uint64_t fp32_rows = __ballot(my_kind == 32);
   sh.qm[row] = my_q;
   if (FIT) sh.iq[row] = my_int ? rn_div(1.0f, my_q) : 0.0f;
   float a_row = 1.0f;
@@ -849,48 +907,46 @@ k_rows(const LaunchArgs P) {
   }
   __builtin_amdgcn_wave_barrier();
 
-  // ---------------- restore (and gate), with the balanced first chain
+  // ---------------- restore (and gate).  R1: every row as an integer row,
+  // R2: pivot rows redone (only when the half has any), R3: the first chain
+  // (u over rows 0..63 in wave 0, the S'^T q part of rows 64..127 in wave 1)
+  // in row order.
   float acc1[2] = {0.0f, 0.0f};
   if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
-    const float *xsh = (w == 0) ? sh.k : sh.q;
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 g4 = lds4(&sh.g[64 * w + 4 * i4]);
-      float4 x4 = {0, 0, 0, 0};
-      if (MODE == MODE_STEP) x4 = lds4(&xsh[64 * w + 4 * i4]);
       const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
-      const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 4 * i4 + e;
-        const uint32_t m = ROW_META(ii);
-        const uint32_t kind = m >> kRowKindShift;
-        const uint32_t off = m & kRowOffMask;
-        const uint32_t d = off >> 5, sft = off & 31u;
-        const uint32_t up = (32u - kind) & 31u;     // integer rows: 24..30
-        uint32_t f[2];
+        const RowProg pr = row_op(uprog, ii);
+        const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const uint32_t lo = codes[d * kDim + l + 64 * c];
-          const uint32_t hi2 = codes[(d + 1) * kDim + l + 64 * c];
-          f[c] = __builtin_amdgcn_alignbit(hi2, lo, sft);
-          // integer code: sign-extend the low `kind` bits with two shifts
-          const int32_t z = (int32_t)(f[c] << up) >> up;
+          const int32_t z = sext_low(__builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pr.xs), pr.z);
           S[c][ii] = ((float)z * gg[e]) * colc[c];
-        }
-        if (kind > 8u) {   // pivot rows (rare): the stored value itself
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            S[c][ii] = gg[e] * (kind == 16u ? __half2float(__ushort_as_half((unsigned short)(f[c] & 0xFFFFu)))
-                                            : __uint_as_float(f[c]));
-        }
-        if (MODE == MODE_STEP) {
-          acc1[0] = __builtin_fmaf(xx[e], S[0][ii], acc1[0]);
-          acc1[1] = __builtin_fmaf(xx[e], S[1][ii], acc1[1]);
         }
       }
       QDR_FENCE();
     }
+    if (pivots != 0) {
+#pragma unroll
+      for (int ii = 0; ii < 64; ++ii) {
+        if ((pivots >> ii) & 1u) {
+          const RowProg pr = row_op(uprog, ii);
+          const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
+          const float gi = sh.g[64 * w + ii];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t f = __builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pr.xs);
+            S[c][ii] = gi * (pr.z == 16u ? __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu)))
+                                         : __uint_as_float(f));
+          }
+        }
+      }
+    }
+    if (MODE == MODE_STEP) chain_rows(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
   }
 
   if (MODE == MODE_UNPACK) {
@@ -950,19 +1006,18 @@ k_rows(const LaunchArgs P) {
     }
   }
 
-  // the staged copy is reused as the output buffer: clear it while the row
-  // factors are computed
-  for (uint32_t off = (uint32_t)l * 16u; off < half_bytes + kDim * 4u; off += 1024u)
-    *reinterpret_cast<uint4 *>(codes8 + off) = make_uint4(0u, 0u, 0u, 0u);
 
   // ---------------- row factors (integer rows only use them)
+  // (the row reduction's scratch aliases the staged words: both waves have
+  // passed the barrier after their restore, so no staged word is read again)
+  float (*red)[20] = reinterpret_cast<float (*)[20]>(codes);
   float r_row = 0.0f, m_row = 0.0f;
   if (SCALE == 0) {
-    m_row = row_reduce<false>(S, sh.red[w], l) * 0.0078125f;
+    m_row = row_reduce<false>(S, red, l) * 0.0078125f;
     const float nu = rn_div(m_row, (P.omega + (size_t)h * kDim)[row]);
     r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
   } else {
-    const float mx = row_reduce<true>(S, sh.red[w], l);
+    const float mx = row_reduce<true>(S, red, l);
     r_row = (mx < FLT_MIN) ? 1.0f : mx;
   }
   if (!my_int) { r_row = 0.0f; m_row = 0.0f; }
@@ -970,7 +1025,6 @@ k_rows(const LaunchArgs P) {
   // excluded from the column maximum (flag 0)
   sh.ir[row] = my_int ? rn_div(1.0f, r_row) : 1.0f;
   sh.m[row] = m_row;
-  if (has_int) store_f32(rs, r_row, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
   __builtin_amdgcn_wave_barrier();
 
   // Y = S / r in place (integer rows), and the column maximum over integer rows
@@ -1013,8 +1067,33 @@ k_rows(const LaunchArgs P) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) ec[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) : 1.0f;
 
-  // ---------------- codes: OR each row's field into the cleared LDS words
+  // ---------------- codes.  Pivot rows first leave their stored bits (fp16
+  // or fp32 of S) in LDS; P1 turns every value into its code bits in place
+  // (straight-line); P2 appends each row's field to the column windows in
+  // row order and stores every completed word.
+  uint32_t *stash = codes;   // [pivot rank][column] (free after the row reduction)
+  if (pivots != 0) {
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) {
+      if ((pivots >> ii) & 1u) {
+        const uint32_t kind = uprog[ii].z;
+        const int rank = __builtin_popcountll(pivots & ((1ull << ii) - 1ull));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          stash[rank * 128 + l + 64 * c] = (kind == 16u) ? (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])))
+                                                       : __float_as_uint(S[c][ii]);
+      }
+    }
+  }
+  // V1a refit sums: fma chains over the integer rows in ascending order, so
+  // wave 1 starts from wave 0's totals over rows 0..63 (it waits for them)
   float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
+  if (FIT && SCALE == 0 && w == 1) {
+    __syncthreads();
+    nacc[0] = sh.d[l]; nacc[1] = sh.d[l + 64];
+    dacc[0] = sh.y[l]; dacc[1] = sh.y[l + 64];
+  }
+  uint32_t (&T)[2][64] = reinterpret_cast<uint32_t (&)[2][64]>(S);   // code bits, in place
 #pragma unroll
   for (int i4 = 0; i4 < 16; ++i4) {
     const float4 q4 = lds4(&sh.qm[64 * w + 4 * i4]);
@@ -1026,80 +1105,99 @@ k_rows(const LaunchArgs P) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ii = 4 * i4 + e;
-      const uint32_t m = ROW_META(ii);
-      const uint32_t kind = m >> kRowKindShift;
-      const uint32_t off = m & kRowOffMask;
-      const uint32_t d = off >> 5, sft = off & 31u;
-      uint32_t f[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const float t = __builtin_fmaf(S[c][ii], ec[c] * qq[e], kMagic);
-        f[c] = __float_as_uint(t);
+        const float y = S[c][ii];
+        const float t = __builtin_fmaf(y, ec[c] * qq[e], kMagic);
         if (FIT) {
           // pivot rows: 1/q is stored as 0, so they add exact zeros
           const float zeta = (t - kMagic) * iqq[e];
           const float pz = mm[e] * zeta;
-          nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
+          nacc[c] = __builtin_fmaf(pz, y, nacc[c]);
           dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
         }
-      }
-      if (kind > 8u) {   // pivot rows (rare)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          f[c] = (kind == 16u) ? (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])))
-                               : __float_as_uint(S[c][ii]);
-      }
-      const uint32_t fmask = (kind == 32u) ? 0xFFFFFFFFu : ((1u << kind) - 1u);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint64_t wide = (uint64_t)(f[c] & fmask) << sft;
-        __hip_atomic_fetch_or(&codes[d * kDim + l + 64 * c], (uint32_t)wide, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_or(&codes[(d + 1) * kDim + l + 64 * c], (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_WORKGROUP);
+        T[c][ii] = __float_as_uint(t);
       }
     }
     QDR_FENCE();
   }
-  __builtin_amdgcn_wave_barrier();
-  // write this half's words back (the padding bits are the cleared zeros)
-  for (uint32_t off = (uint32_t)l * 16u; off < half_bytes; off += 1024u) {
-    const uint4 t = *reinterpret_cast<const uint4 *>(codes8 + off);
-    store_granule(rs, t, off, half_off);
+  if (FIT && SCALE == 0 && w == 0) {
+    sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
+    sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];
+    __syncthreads();
+  }
+  if (pivots != 0) {
+    // pivot rows: their stored bits replace the code bits
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ii = 0; ii < 64; ++ii) {
+      if ((pivots >> ii) & 1u) {
+        const int rank = __builtin_popcountll(pivots & ((1ull << ii) - 1ull));
+        T[0][ii] = stash[rank * 128 + l];
+        T[1][ii] = stash[rank * 128 + l + 64];
+      }
+    }
+  }
+  {
+    // the completed words go to the wave's LDS region (the stash has been
+    // read), then out with 16-byte stores, 1 KiB of the half per instruction
+    uint32_t win[2] = {0u, 0u};   // the last 32 stream bits written, per column
+    if (fp32_rows == 0) {
+      // every field is at most 16 bits wide: straight-line appends.  The word
+      // a field ends in is written whether or not the field completes it; a
+      // word that is not yet complete is rewritten by the field that
+      // completes it (or by the final flush), later in program order.
+#pragma unroll
+      for (int ii = 0; ii < 64; ++ii) {
+        const RowProg pr = row_op(pprog, ii);
+        uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
+        o[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], pr.xs);
+        o[64] = __builtin_amdgcn_alignbit(T[1][ii], win[1], pr.xs);
+        win[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], pr.z);
+        win[1] = __builtin_amdgcn_alignbit(T[1][ii], win[1], pr.z);
+      }
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 64; ++ii) {
+        const RowProg pr = row_op(uprog, ii);
+        const uint32_t off = ((pr.xs & ~511u) >> 4) + (pr.xs & 31u);   // stream bit of the field in this half
+        if (pr.z == 32u) {   // an FP32 row: its two 16-bit halves in turn
+          append_field(codes, l, win, T[0][ii], T[1][ii], off, 16u);
+          append_field(codes, l, win, T[0][ii] >> 16, T[1][ii] >> 16, off + 16u, 16u);
+        } else {
+          append_field(codes, l, win, T[0][ii], T[1][ii], off, pr.z);
+        }
+      }
+    }
+    // a partly filled last word: its bits sit at the top of the window;
+    // shift them down with zeros above (the padding of the half)
+    const RowProg plast = row_op(uprog, 63);
+    const uint32_t end = ((plast.xs & ~511u) >> 4) + (plast.xs & 31u) + plast.z;
+    const uint32_t rem = end & 31u;
+    if (rem != 0u) {
+      uint32_t *o = codes + (end >> 5) * kDim + l;
+      o[0] = __builtin_amdgcn_alignbit(0u, win[0], 32u - rem);
+      o[64] = __builtin_amdgcn_alignbit(0u, win[1], 32u - rem);
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (uint32_t boff = (uint32_t)l * 16u; boff < half_bytes; boff += 1024u)
+      store_granule(rs, *reinterpret_cast<const uint4 *>(codes8 + boff), boff, half_off);
   }
 
-  // ---------------- column factor
+  // ---------------- row and column factors (stored after every read of the
+  // row tables, so those stay scalar loads)
+  if (has_int) store_f32(rs, r_row, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
   if (SCALE == 0 && has_int) {
     if (!FIT) {
       if (w == 0) {
         store_f32(rs, c0[0], (uint32_t)l * 4u, c_off);
         store_f32(rs, c0[1], (uint32_t)l * 4u + 256u, c_off);
       }
-    } else {
-      if (w == 0) {
-        sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
-        sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];
-      }
-      __syncthreads();
-      if (w == 1) {
+    } else if (w == 1) {
+      // wave 1 holds the sums over all integer rows
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          // wave 1's own sums started from zero; redo them from wave 0's
-          float nn = sh.d[l + 64 * c], dd = sh.y[l + 64 * c];
-#pragma unroll
-          for (int ii = 0; ii < 64; ++ii) {
-            const float qm = sh.qm[64 + ii];
-            if (qm > 0.0f) {
-              const float t = __builtin_fmaf(S[c][ii], ec[c] * qm, kMagic);
-              const float zeta = (t - kMagic) * rn_div(1.0f, qm);
-              const float pz = sh.m[64 + ii] * zeta;
-              nn = __builtin_fmaf(pz, S[c][ii], nn);
-              dd = __builtin_fmaf(pz, zeta, dd);
-            }
-          }
-          store_f32(rs, (dd > 0.0f) ? rn_div(nn, dd) : c0[c], (uint32_t)l * 4u + 256u * c, c_off);
-        }
-      }
+      for (int c = 0; c < 2; ++c)
+        store_f32(rs, (dacc[c] > 0.0f) ? rn_div(nacc[c], dacc[c]) : c0[c], (uint32_t)l * 4u + 256u * c, c_off);
     }
   }
 
@@ -1110,7 +1208,6 @@ k_rows(const LaunchArgs P) {
     orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
     orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
   }
-#undef ROW_META
 }
 
 // --------------------------------------------------------------------------

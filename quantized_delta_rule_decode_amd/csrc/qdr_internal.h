@@ -32,10 +32,21 @@ struct ListEntry {
 };
 static_assert(sizeof(HeadInfo) == 16 && sizeof(ListEntry) == 32, "device table layout");
 
-// Row units: per (head, row) word = bit offset of the row inside its half of
-// the column stream (bits 0..15) | kind (bits 16..23).
-constexpr uint32_t kRowOffMask = 0xFFFFu;
-constexpr int kRowKindShift = 16;
+// Row units: two tables with one entry per (head, row) describing the row's
+// field in its half of the column streams, as operands the kernel uses
+// directly (each entry is one 8-byte scalar load; no per-row scalar
+// arithmetic runs on the device).  With x = byte offset of the field's first
+// 32-bit word in the half's [word][column] image (word index * 512, so its
+// low 9 bits are zero), y = bit offset of the field in that word and
+// z = the field's width (the row's kind):
+//   unpack entry: {x | y, z}            (restore: funnel shift by y)
+//   pack entry:   {x | ((32 - y) & 31), z}  (repack: completing shift)
+// A funnel shift reads only the low 5 bits of its shift operand, and the
+// LDS address is (x | y) with the low 9 bits replaced by the lane's byte.
+struct RowProg {
+  uint32_t xs;   // x | shift
+  uint32_t z;    // width
+};
 
 // Everything a launch needs, passed by value as the kernel argument.
 struct LaunchArgs {
@@ -45,8 +56,9 @@ struct LaunchArgs {
   int32_t H;
   const ListEntry *head_list;   // heads handled by this launch
   int32_t n_list;
-  const uint32_t *row_meta;   // [H*128] (row units), see kRowOffMask
-  int32_t half_words;         // row units: LDS words reserved per column and half
+  const RowProg *row_unpack;  // [H*128] (row units)
+  const RowProg *row_pack;    // [H*128] (row units)
+  int32_t region_rows;        // row units: LDS rows of 128 words in each wave's region
   const float *omega;         // [H*128]
   uint32_t *err;              // device error word
   const int32_t *slots;       // [n] slot of each request / dense entry
@@ -59,6 +71,7 @@ struct LaunchArgs {
 struct PoolConfig {
   int unit, gate, scale_mode, fit_iters;
   int max_words;              // row units: largest words-per-column of any half
+  int max_pivots;             // row units: most FP16/FP32 rows in any half
 };
 
 // Whole-head launches.  Integer kinds share one launch per mode

@@ -1,4 +1,6 @@
 // qdr_rows.hip -- row-unit kernels (per-key-row storage kinds) and their launch.
+#include <algorithm>
+
 #include "qdr_device.h"
 
 namespace qdr {
@@ -10,10 +12,14 @@ hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const ListEnt
                        hipStream_t st) {
   a.head_list = list;
   a.n_list = count;
-  a.half_words = cfg.max_words;
+  // Each wave's LDS region (rows of 128 words): the staged words of its half
+  // plus one row (the second word of a funnel shift), reused after the
+  // restore as the row reduction's scratch (64 x 20 floats = 10 rows) and for
+  // the stored bits of the half's pivot rows (one row each).
+  a.region_rows = std::max({cfg.max_words + 1, cfg.max_pivots, 10});
+  const size_t lds = (size_t)2 * a.region_rows * kDim * sizeof(uint32_t);
   const dim3 grid((unsigned)((int64_t)n * count)), block(128);
   if (grid.x == 0) return hipSuccess;
-  const size_t lds = (size_t)2 * (cfg.max_words + 1) * kDim * sizeof(uint32_t);
   const bool dual = cfg.scale_mode == 0, fit = cfg.fit_iters > 0, diag = cfg.gate == 1;
   if (lds > 65536) {   // pools with FP32 rows: allow the larger dynamic LDS
     const void *fns[6] = {(const void *)k_rows<MODE, 1, 1, 0>, (const void *)k_rows<MODE, 0, 1, 0>,

@@ -63,10 +63,11 @@ struct HostLayout {
   std::vector<uint64_t> head_off;
   std::vector<uint32_t> head_bytes, code_bytes;
   std::vector<uint8_t> words0, words1; // row units: words per column and half
-  std::vector<uint32_t> row_meta;     // row units: [H*128]
+  std::vector<qdr::RowProg> row_unpack, row_pack;  // row units: [H*128] each
   std::vector<uint8_t> has_scales;
   uint64_t slot_stride = 0;
   int max_words = 0;
+  int max_pivots = 0;                 // row units: most float rows in one half
   double stored_bits = 0;             // per slot
 };
 
@@ -112,23 +113,33 @@ void build_layout(const qdr_pool_desc *d, HostLayout &L) {
   L.words0.resize(H);
   L.words1.resize(H);
   L.has_scales.resize(H);
-  if (d->unit == QDR_UNIT_ROW) L.row_meta.resize((size_t)H * QDR_DIM);
+  if (d->unit == QDR_UNIT_ROW) {
+    L.row_unpack.resize((size_t)H * QDR_DIM);
+    L.row_pack.resize((size_t)H * QDR_DIM);
+  }
   uint64_t off = 0;
   double bits = 0;
   L.max_words = 0;
+  L.max_pivots = 0;
   const uint64_t G = d->unit == QDR_UNIT_HEAD ? 16 : 4;
   for (int h = 0; h < H; ++h) {
     uint64_t ng = 0;
     bool any_int = false;
     for (int half = 0; half < 2; ++half) {
       uint64_t hbits = 0;
+      int npiv = 0;
       for (int i = 64 * half; i < 64 * half + 64; ++i) {
         const int k = d->unit == QDR_UNIT_HEAD ? d->kinds[h] : d->kinds[(size_t)h * QDR_DIM + i];
-        if (d->unit == QDR_UNIT_ROW)
-          L.row_meta[(size_t)h * QDR_DIM + i] = (uint32_t)hbits | ((uint32_t)k << qdr::kRowKindShift);
+        if (d->unit == QDR_UNIT_ROW) {
+          const uint32_t x = (uint32_t)(hbits >> 5) * (QDR_DIM * 4u), y = (uint32_t)(hbits & 31u);
+          L.row_unpack[(size_t)h * QDR_DIM + i] = {x | y, (uint32_t)k};
+          L.row_pack[(size_t)h * QDR_DIM + i] = {x | ((32u - y) & 31u), (uint32_t)k};
+        }
         hbits += (uint64_t)k;
         any_int = any_int || is_int_kind(k);
+        npiv += is_int_kind(k) ? 0 : 1;
       }
+      if (npiv > L.max_pivots) L.max_pivots = npiv;
       const uint64_t hg = (hbits + 8 * G - 1) / (8 * G);
       ng += hg;
       const int words = (int)(hg * G / 4);
@@ -160,7 +171,7 @@ struct qdr_pool {
   int device = 0;
   uint8_t *base = nullptr;
   bool owns_base = false;
-  uint32_t *d_row_meta = nullptr;
+  qdr::RowProg *d_row_unpack = nullptr, *d_row_pack = nullptr;
   float *d_omega = nullptr;
   uint32_t *d_err = nullptr;
   qdr::ListEntry *d_lists[qdr::kNumLists] = {};
@@ -200,7 +211,8 @@ std::vector<qdr::ListEntry> interleave_int_heads(const std::vector<std::vector<q
 void free_pool(qdr_pool *p) {
   if (!p) return;
   if (p->owns_base && p->base) (void)hipFree(p->base);
-  (void)hipFree(p->d_row_meta);
+  (void)hipFree(p->d_row_unpack);
+  (void)hipFree(p->d_row_pack);
   (void)hipFree(p->d_omega);
   (void)hipFree(p->d_err);
   for (auto &l : p->d_lists) (void)hipFree(l);
@@ -213,7 +225,8 @@ qdr::LaunchArgs base_args(const qdr_pool *p) {
   a.slot_stride = p->L.slot_stride;
   a.num_slots = p->desc.num_slots;
   a.H = p->desc.num_heads;
-  a.row_meta = p->d_row_meta;
+  a.row_unpack = p->d_row_unpack;
+  a.row_pack = p->d_row_pack;
   a.omega = p->d_omega;
   a.err = p->d_err;
   return a;
@@ -280,6 +293,7 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
   p->cfg.scale_mode = desc->scale_mode;
   p->cfg.fit_iters = desc->fit_iters;
   p->cfg.max_words = p->L.max_words;
+  p->cfg.max_pivots = p->L.max_pivots;
   if (hipGetDevice(&p->device) != hipSuccess) { free_pool(p); return fail(QDR_E_DEVICE, "no HIP device"); }
 
   const uint64_t total = p->L.slot_stride * (uint64_t)desc->num_slots;
@@ -315,7 +329,8 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
   hipError_t e = hipMemset(p->base, 0, total);
   if (e == hipSuccess) e = upload(&p->d_omega, p->omega.data(), p->omega.size());
   if (e == hipSuccess && desc->unit == QDR_UNIT_ROW) {
-    e = upload(&p->d_row_meta, p->L.row_meta.data(), p->L.row_meta.size());
+    e = upload(&p->d_row_unpack, p->L.row_unpack.data(), p->L.row_unpack.size());
+    if (e == hipSuccess) e = upload(&p->d_row_pack, p->L.row_pack.data(), p->L.row_pack.size());
   }
   for (int i = 0; i < qdr::kNumLists && e == hipSuccess; ++i) {
     p->list_count[i] = (int32_t)lists[i].size();

@@ -928,8 +928,7 @@ k_rows(const LaunchArgs P) {
           S[c][ii] = ((float)z * gg[e]) * colc[c];
         }
       }
-      QDR_FENCE();
-    }
+          }
     if (pivots != 0) {
 #pragma unroll
       for (int ii = 0; ii < 64; ++ii) {
@@ -1002,8 +1001,7 @@ k_rows(const LaunchArgs P) {
         S[0][ii] = __builtin_fmaf(bb[e], dl[0], S[0][ii]);
         S[1][ii] = __builtin_fmaf(bb[e], dl[1], S[1][ii]);
       }
-      QDR_FENCE();
-    }
+          }
   }
 
 
@@ -1047,8 +1045,7 @@ k_rows(const LaunchArgs P) {
         cm[c] = fmaxf(cm[c], (qq[e] > 0.0f) ? fabsf(y) : 0.0f);
       }
     }
-    QDR_FENCE();
-  }
+      }
   float c0[2] = {1.0f, 1.0f};
   if (SCALE == 0) {
     sh.cmax[w][l] = cm[0];
@@ -1119,8 +1116,7 @@ k_rows(const LaunchArgs P) {
         T[c][ii] = __float_as_uint(t);
       }
     }
-    QDR_FENCE();
-  }
+      }
   if (FIT && SCALE == 0 && w == 0) {
     sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
     sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];

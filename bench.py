@@ -110,6 +110,46 @@ def fp32_comparator(cfg, f32_pool, inputs, o, reps: int = 4):
             "state": "fp32, 64 KiB per head, same kernel family (whole-head FP32 kind)"}
 
 
+def fp32_trajectory_error(cid: int):
+    """Error of the quantised decode trajectory against the unquantised delta
+    rule on the same inputs: config `cid`'s pool and an FP32-kind pool start
+    from the same state (the FP32 warm-up packed, or zero) and take the
+    config's decode steps; relative L2 of the readouts over all steps and of
+    the final states (the quantised one restored by qdr_unpack)."""
+    import torch
+    from quantized_delta_rule_decode_amd import qdr, synth, workload
+    cfg = synth.CONFIGS[cid]
+    tables = synth.static_tables(cfg)
+    dev = torch.device("cuda")
+    pool = workload.make_pool(cfg, tables)
+    slots = torch.from_numpy(tables["slots"]).to(dev)
+    ident = torch.arange(cfg.B, dtype=torch.int32, device=dev)
+    if cfg.warmup > 0:
+        ref = workload.warm_start(cfg, tables, pool, slots, cfg.warmup)
+    else:
+        ref = workload.fp32_pool(cfg, cfg.B)
+        ref.qdr_slot_reset(ident)
+        pool.qdr_slot_reset(slots)
+    o = torch.empty((cfg.B, cfg.H, qdr.DIM), dtype=torch.float32, device=dev)
+    o32 = torch.empty_like(o)
+    num = den = 0.0
+    for t in range(cfg.steps):
+        q, k, v, beta, gate = workload.step_inputs(cfg, tables, t)
+        pool.qdr_decode_step(slots, q, k, v, beta, gate, o)
+        ref.qdr_decode_step(ident, q, k, v, beta, gate, o32)
+        num += float((o.double() - o32.double()).square().sum())
+        den += float(o32.double().square().sum())
+    S = torch.empty((cfg.B, cfg.H, qdr.DIM, qdr.DIM), dtype=torch.float32, device=dev)
+    S32 = torch.empty_like(S)
+    pool.qdr_unpack(slots, S)
+    ref.qdr_unpack(ident, S32)
+    st = float((S.double() - S32.double()).norm() / S32.double().norm())
+    assert pool.qdr_poll_device_error() == 0 and ref.qdr_poll_device_error() == 0
+    pool.close()
+    ref.close()
+    return {"workload": cfg.name, "steps": cfg.steps, "o_rel_l2": (num / den) ** 0.5, "final_state_rel_l2": st}
+
+
 def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
     """HBM rate of a plain in-place streaming kernel on this GPU (torch add_ of
     an fp32 buffer: each byte read once and written once), for scale."""
@@ -133,6 +173,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-comparator", action="store_true",
                     help="skip timing the FP32-state pool of the warm-up")
+    ap.add_argument("--no-trajectory-error", action="store_true",
+                    help="skip the quantised-vs-FP32 trajectory error of the small configs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -199,6 +241,7 @@ def main():
     value = head_steps / (gpu_ms * 1e-3)
 
     stream = stream_reference()
+    traj = None if args.no_trajectory_error else [fp32_trajectory_error(c) for c in (1, 2, 3)]
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(os.cpu_count() or 1, 16)
@@ -236,6 +279,7 @@ def main():
                      "frac_of_stream_reference": achieved / stream["GBps"]},
         "fp32_state_comparator": None if fp32_cmp is None else {
             **fp32_cmp, "speedup_packed_over_fp32": fp32_cmp["ms_per_step"] / gpu_ms},
+        "fp32_trajectory_error": traj,
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "setup_s": setup_s,

@@ -150,6 +150,50 @@ def fp32_trajectory_error(cid: int):
     return {"workload": cfg.name, "steps": cfg.steps, "o_rel_l2": (num / den) ** 0.5, "final_state_rel_l2": st}
 
 
+def two_stream_split(pool, slots, inputs, o, fused_ms: float, reps: int = 5):
+    """qdr_decode_step_split on the benchmark pool: how soon o is ready (the
+    readout launches on their stream) and the whole split step, with and
+    without a stand-in for downstream model work (an fp32 matmul chain) queued
+    on the readout stream right after o, against the fused step followed by
+    the same work on one stream."""
+    import torch
+    sr, sw = torch.cuda.Stream(), torch.cuda.Stream()
+    a = torch.randn((4096, 4096), device="cuda")
+    b = torch.randn((4096, 4096), device="cuda")
+
+    def model_work(stream):
+        with torch.cuda.stream(stream):
+            c = a
+            for _ in range(2):
+                c = torch.mm(c, b)
+        return c
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def one(with_work: bool):
+        torch.cuda.synchronize()
+        ev[0].record(sr)
+        pool.qdr_decode_step_split(slots, *inputs, o, sr, sw)
+        ev[1].record(sr)
+        if with_work:
+            model_work(sr)
+        sw.wait_stream(sr)
+        ev[2].record(sw)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]), ev[0].elapsed_time(ev[2])
+
+    one(True)
+    ro = [one(False) for _ in range(reps)]
+    wk = [one(True) for _ in range(reps)]
+    cur = torch.cuda.current_stream()
+    work_ms = time_on_stream(lambda: model_work(cur), reps)
+    serial_ms = time_on_stream(lambda: (pool.qdr_decode_step(slots, *inputs, o), model_work(cur)), reps)
+    return {"readout_ms": float(np.mean([r[0] for r in ro])), "split_total_ms": float(np.mean([r[1] for r in ro])),
+            "fused_ms": fused_ms, "model_work": "2 x fp32 matmul 4096^3 on the readout stream after o",
+            "model_work_ms": work_ms, "fused_then_work_ms": serial_ms,
+            "split_with_work_ms": float(np.mean([r[1] for r in wk]))}
+
+
 def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
     """HBM rate of a plain in-place streaming kernel on this GPU (torch add_ of
     an fp32 buffer: each byte read once and written once), for scale."""
@@ -173,6 +217,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-comparator", action="store_true",
                     help="skip timing the FP32-state pool of the warm-up")
+    ap.add_argument("--no-split", action="store_true", help="skip timing the two-stream step")
     ap.add_argument("--no-trajectory-error", action="store_true",
                     help="skip the quantised-vs-FP32 trajectory error of the small configs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -240,6 +285,8 @@ def main():
     achieved = nbytes / (gpu_ms * 1e-3) / 1e9
     value = head_steps / (gpu_ms * 1e-3)
 
+    split = None if args.no_split else two_stream_split(pool, slots, (q, k, v, beta, gate), o, gpu_ms)
+    assert pool.qdr_poll_device_error() == 0
     stream = stream_reference()
     traj = None if args.no_trajectory_error else [fp32_trajectory_error(c) for c in (1, 2, 3)]
     cpu = None
@@ -279,6 +326,7 @@ def main():
                      "frac_of_stream_reference": achieved / stream["GBps"]},
         "fp32_state_comparator": None if fp32_cmp is None else {
             **fp32_cmp, "speedup_packed_over_fp32": fp32_cmp["ms_per_step"] / gpu_ms},
+        "two_stream_split": split,
         "fp32_trajectory_error": traj,
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,

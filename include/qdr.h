@@ -158,6 +158,26 @@ qdr_status qdr_decode_step(qdr_pool *pool, const int32_t *slots, int32_t B,
                            const float *beta, const float *gate, float *o,
                            void *stream);
 
+/* The same step split over two streams (Tutorial §四, engineering paragraph:
+ * the head output goes downstream first, and a second stream writes the
+ * compressed state back so that the scale update overlaps model compute).
+ *   1. on stream_readout: restore, gate, u and delta, o = S_t^T q -> o (the
+ *      state is not written);
+ *   2. on stream_writeback, ordered after 1 by an event: the whole step again
+ *      (restore, update, refit, requantise, store) without writing o.
+ * o and the stored state are bit-identical to qdr_decode_step's.  The
+ * inputs (slots, q, k, v, beta, gate) must stay unchanged until
+ * stream_writeback has finished.  Every later call on this pool, on any
+ * stream, is ordered after the write-back by the library (an event recorded
+ * on stream_writeback; qdr_read_raw / qdr_write_raw included).  Both streams
+ * belong to the caller and must have the default priority; they may be the
+ * same stream.  Calls on one pool from several host threads at once race.
+ * Errors as qdr_decode_step, plus QDR_E_DEVICE if an event call fails. */
+qdr_status qdr_decode_step_split(qdr_pool *pool, const int32_t *slots, int32_t B,
+                                 const float *q, const float *k, const float *v,
+                                 const float *beta, const float *gate, float *o,
+                                 void *stream_readout, void *stream_writeback);
+
 /* Layout of the pool (pointers stay valid until qdr_pool_destroy). */
 qdr_status qdr_get_layout(const qdr_pool *pool, qdr_layout *out);
 

@@ -366,6 +366,7 @@ struct Shared : SharedCore {
 // --------------------------------------------------------------------------
 // Whole-head kernel: every row of the head has kind BITS.
 // MODE_STEP: restore, gate, delta update, readout, requantise, store.
+// MODE_READOUT: restore, gate, u and delta, readout only (no store).
 // MODE_PACK: requantise S_in.  MODE_UNPACK: restore into S_out.
 // MODE_RESET: requantise S = 0.
 // --------------------------------------------------------------------------
@@ -401,7 +402,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   if (slot < 0 || slot >= P.num_slots) {
     if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
-    if (MODE == MODE_STEP && w == 0) {
+    if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
       P.o[bh * kDim + l] = 0.0f;     // wave 0 and 1 cover columns 0..127
       P.o[bh * kDim + 64 + l] = 0.0f;
     }
@@ -423,7 +424,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   // ---------------- load codes (both columns of this lane, this wave's rows)
   uint32_t wd[2][K::NW];
-  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -436,10 +437,10 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   // ---------------- per-row scalars of this lane's row, broadcast via LDS
   float a_row = 1.0f;
-  if (MODE == MODE_STEP) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
     a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
   }
-  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
     if (INT) {
       const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
       sh.g[row] = (a_row * rn_div(r_row, QMAX)) * GSCALE;
@@ -452,7 +453,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     }
   }
   float vcol[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
     const float kr = (P.k + bh * kDim)[row];
     sh.k[row] = kr;
     sh.b[row] = P.beta[bh] * kr;
@@ -469,7 +470,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   // wave 0 runs its half of u inside the restore and its q part after the
   // hand-off, wave 1 the other way round.
   float acc1[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP)
+  if (MODE == MODE_STEP || MODE == MODE_READOUT)
     restore_rows<BITS, true, OFF4>(S, acc1, wd, colc, sh.g, (w == 0) ? sh.k : sh.q, 64 * w);
   else if (MODE == MODE_UNPACK)
     restore_rows<BITS, false, OFF4>(S, acc1, wd, colc, sh.g, sh.g, 64 * w);
@@ -500,7 +501,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   // ---------------- delta update
   float oq[2] = {0.0f, 0.0f};
   float dl[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
     if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
     const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
     if (l == 0) sh.qb[w] = qb_part;
@@ -518,6 +519,19 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     __syncthreads();
     dl[0] = sh.d[l];
     dl[1] = sh.d[l + 64];
+    if constexpr (MODE == MODE_READOUT) {
+      // readout-first launch: o = S'^T q + (q . b) delta as in the step;
+      // the state is neither updated nor stored (the write-back launch does it)
+      if (w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
+      __syncthreads();
+      if (w == 0 && P.o != nullptr) {
+        const float qb_all = sh.qb[0] + sh.qb[1];
+        float *orow = P.o + bh * kDim;
+        orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
+        orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
+      }
+      return;
+    }
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
@@ -690,7 +704,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   }
 
   // ---------------- the readout
-  if (MODE == MODE_STEP && w == 0) {
+  if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
     const float qb_all = sh.qb[0] + sh.qb[1];
     float *orow = P.o + bh * kDim;
     orow[l] = (ocol[0] + sh.x[l]) + qb_all * dl[0];
@@ -834,7 +848,7 @@ k_rows(const LaunchArgs P) {
 
   if (slot < 0 || slot >= P.num_slots) {
     if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
-    if (MODE == MODE_STEP && w == 0) {
+    if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
       float *orow = P.o + bh * kDim;
       orow[l] = 0.0f;
       orow[l + 64] = 0.0f;
@@ -865,7 +879,7 @@ k_rows(const LaunchArgs P) {
   float colc[2] = {1.0f, 1.0f};
 
   // ---------------- stage this half's code words in LDS (1 KiB per wave instruction)
-  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
     for (uint32_t boff = (uint32_t)l * 16u; boff < half_bytes; boff += 1024u)
       *reinterpret_cast<uint4 *>(codes8 + boff) = load_granule(rs, boff, half_off);
     codes[nwords * kDim + l] = 0u;
@@ -882,8 +896,8 @@ k_rows(const LaunchArgs P) {
   sh.qm[row] = my_q;
   if (FIT) sh.iq[row] = my_int ? rn_div(1.0f, my_q) : 0.0f;
   float a_row = 1.0f;
-  if (MODE == MODE_STEP) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
-  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
+  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
     if (my_int) {
       const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
       sh.g[row] = a_row * rn_div(r_row, my_q);
@@ -896,7 +910,7 @@ k_rows(const LaunchArgs P) {
     }
   }
   float vcol[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
     const float kr = (P.k + bh * kDim)[row];
     sh.k[row] = kr;
     sh.b[row] = P.beta[bh] * kr;
@@ -912,7 +926,7 @@ k_rows(const LaunchArgs P) {
   // (u over rows 0..63 in wave 0, the S'^T q part of rows 64..127 in wave 1)
   // in row order.
   float acc1[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP || MODE == MODE_UNPACK) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 g4 = lds4(&sh.g[64 * w + 4 * i4]);
@@ -945,7 +959,7 @@ k_rows(const LaunchArgs P) {
         }
       }
     }
-    if (MODE == MODE_STEP) chain_rows(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
+    if (MODE == MODE_STEP || MODE == MODE_READOUT) chain_rows(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
   }
 
   if (MODE == MODE_UNPACK) {
@@ -973,7 +987,7 @@ k_rows(const LaunchArgs P) {
   // ---------------- delta update (same hand-off as k_head)
   float oq[2] = {0.0f, 0.0f};
   float dl[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP) {
+  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
     if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
     const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
     if (l == 0) sh.qb[w] = qb_part;
@@ -991,6 +1005,19 @@ k_rows(const LaunchArgs P) {
     __syncthreads();
     dl[0] = sh.d[l];
     dl[1] = sh.d[l + 64];
+    if constexpr (MODE == MODE_READOUT) {
+      // readout-first launch: o = S'^T q + (q . b) delta as in the step;
+      // the state is neither updated nor stored (the write-back launch does it)
+      if (w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
+      __syncthreads();
+      if (w == 0 && P.o != nullptr) {
+        const float qb_all = sh.qb[0] + sh.qb[1];
+        float *orow = P.o + bh * kDim;
+        orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
+        orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
+      }
+      return;
+    }
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
@@ -1198,7 +1225,7 @@ k_rows(const LaunchArgs P) {
   }
 
   // ---------------- readout
-  if (MODE == MODE_STEP && w == 0) {
+  if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
     const float qb_all = sh.qb[0] + sh.qb[1];
     float *orow = P.o + bh * kDim;
     orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
@@ -1259,6 +1286,7 @@ template <int BITS>
 hipError_t launch_head_modes(const PoolConfig &cfg, const LaunchArgs &a, int n, int mode, hipStream_t st) {
   switch (mode) {
     case MODE_STEP: return launch_head_kind<BITS, MODE_STEP>(cfg, a, n, st);
+    case MODE_READOUT: return launch_head_kind<BITS, MODE_READOUT>(cfg, a, n, st);
     case MODE_PACK: return launch_head_kind<BITS, MODE_PACK>(cfg, a, n, st);
     case MODE_UNPACK: return launch_head_kind<BITS, MODE_UNPACK>(cfg, a, n, st);
     default: return launch_head_kind<BITS, MODE_RESET>(cfg, a, n, st);

@@ -11,7 +11,7 @@ namespace qdr {
 
 constexpr int kDim = 128;
 
-enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3 };
+enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3, MODE_READOUT = 4 };
 
 // Per-head metadata on the device (16 bytes).
 struct HeadInfo {
@@ -82,6 +82,7 @@ hipError_t launch_head_int_step(const PoolConfig &, const LaunchArgs &, int n, h
 hipError_t launch_head_int_pack(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_int_unpack(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_int_reset(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
+hipError_t launch_head_int_readout(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_b16(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 hipError_t launch_head_b32(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 // Row-unit launch (qdr_rows.hip) over the heads in list[0..count).

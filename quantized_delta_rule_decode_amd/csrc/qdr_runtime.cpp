@@ -176,6 +176,10 @@ struct qdr_pool {
   uint32_t *d_err = nullptr;
   qdr::ListEntry *d_lists[qdr::kNumLists] = {};
   int32_t list_count[qdr::kNumLists] = {};
+  // two-stream step: recorded on the write-back stream after its launches;
+  // every later call on the pool orders its stream after it
+  hipEvent_t wb_done = nullptr;
+  bool wb_recorded = false;
 };
 
 namespace {
@@ -216,6 +220,7 @@ void free_pool(qdr_pool *p) {
   (void)hipFree(p->d_omega);
   (void)hipFree(p->d_err);
   for (auto &l : p->d_lists) (void)hipFree(l);
+  if (p->wb_done) (void)hipEventDestroy(p->wb_done);
   delete p;
 }
 
@@ -250,7 +255,16 @@ qdr_status check_slots_host(const qdr_pool *p, const int32_t *slots, int32_t n, 
   return QDR_OK;
 }
 
+// Order `st` after the last two-stream write-back on this pool (a no-op when
+// there has been none; waiting on a completed event costs nothing).
+hipError_t after_writeback(qdr_pool *p, hipStream_t st) {
+  if (!p->wb_recorded) return hipSuccess;
+  return hipStreamWaitEvent(st, p->wb_done, 0);
+}
+
 qdr_status dispatch(qdr_pool *p, qdr::LaunchArgs a, int n, int mode, hipStream_t st) {
+  const hipError_t we = after_writeback(p, st);
+  if (we != hipSuccess) return fail(QDR_E_DEVICE, "stream wait failed: %s", hipGetErrorString(we));
   const qdr::ListEntry *lists[qdr::kNumLists];
   for (int i = 0; i < qdr::kNumLists; ++i) lists[i] = p->d_lists[i];
   hipError_t e = qdr::launch_all(p->cfg, a, n, lists, p->list_count, mode, st);
@@ -406,6 +420,51 @@ qdr_status qdr_decode_step(qdr_pool *pool, const int32_t *slots, int32_t B, cons
   return dispatch(pool, a, B, qdr::MODE_STEP, st);
 }
 
+qdr_status qdr_decode_step_split(qdr_pool *pool, const int32_t *slots, int32_t B, const float *q, const float *k,
+                                 const float *v, const float *beta, const float *gate, float *o,
+                                 void *stream_readout, void *stream_writeback) {
+  if (!pool) return fail(QDR_E_INVAL, "pool is NULL");
+  if (B < 0) return fail(QDR_E_INVAL, "B must be >= 0");
+  if (B == 0) return ok();
+  if (!slots || !q || !k || !v || !beta || !gate || !o)
+    return fail(QDR_E_INVAL, "a tensor pointer is NULL");
+  hipStream_t sr = static_cast<hipStream_t>(stream_readout);
+  hipStream_t sw = static_cast<hipStream_t>(stream_writeback);
+  qdr_status cs = check_slots_host(pool, slots, B, sr, true);
+  if (cs != QDR_OK) return cs;
+  if (!pool->wb_done) {
+    const hipError_t e = hipEventCreateWithFlags(&pool->wb_done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      pool->wb_done = nullptr;
+      return fail(QDR_E_DEVICE, "event create failed: %s", hipGetErrorString(e));
+    }
+  }
+  qdr::LaunchArgs a = base_args(pool);
+  a.slots = slots;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.gate = gate;
+  a.o = o;
+  // 1. readout-first launches on stream_readout (ordered after any earlier write-back)
+  qdr_status st = dispatch(pool, a, B, qdr::MODE_READOUT, sr);
+  if (st != QDR_OK) return st;
+  // 2. the write-back launches on stream_writeback, after the readout has read
+  //    the codes they overwrite; the full step without the o store
+  hipError_t e = hipEventRecord(pool->wb_done, sr);
+  if (e == hipSuccess) e = hipStreamWaitEvent(sw, pool->wb_done, 0);
+  if (e != hipSuccess) return fail(QDR_E_DEVICE, "stream ordering failed: %s", hipGetErrorString(e));
+  a.o = nullptr;
+  st = dispatch(pool, a, B, qdr::MODE_STEP, sw);
+  if (st != QDR_OK) return st;
+  // 3. later calls on this pool, on any stream, wait for the write-back
+  e = hipEventRecord(pool->wb_done, sw);
+  if (e != hipSuccess) return fail(QDR_E_DEVICE, "event record failed: %s", hipGetErrorString(e));
+  pool->wb_recorded = true;
+  return ok();
+}
+
 qdr_status qdr_get_layout(const qdr_pool *pool, qdr_layout *out) {
   if (!pool || !out) return fail(QDR_E_INVAL, "pool or out is NULL");
   out->slot_stride = pool->L.slot_stride;
@@ -425,7 +484,8 @@ qdr_status qdr_read_raw(qdr_pool *pool, int32_t slot, void *host_dst, size_t n, 
   if (slot < 0 || slot >= pool->desc.num_slots) return fail(QDR_E_SLOT, "slot %d out of range", slot);
   if (n != pool->L.slot_stride) return fail(QDR_E_INVAL, "n must equal slot_stride (%llu)", (unsigned long long)pool->L.slot_stride);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(host_dst, pool->base + (size_t)slot * pool->L.slot_stride, n, hipMemcpyDeviceToHost, st);
+  hipError_t e = after_writeback(pool, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_dst, pool->base + (size_t)slot * pool->L.slot_stride, n, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(QDR_E_DEVICE, "read_raw: %s", hipGetErrorString(e));
   return ok();
@@ -436,7 +496,8 @@ qdr_status qdr_write_raw(qdr_pool *pool, int32_t slot, const void *host_src, siz
   if (slot < 0 || slot >= pool->desc.num_slots) return fail(QDR_E_SLOT, "slot %d out of range", slot);
   if (n != pool->L.slot_stride) return fail(QDR_E_INVAL, "n must equal slot_stride (%llu)", (unsigned long long)pool->L.slot_stride);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(pool->base + (size_t)slot * pool->L.slot_stride, host_src, n, hipMemcpyHostToDevice, st);
+  hipError_t e = after_writeback(pool, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(pool->base + (size_t)slot * pool->L.slot_stride, host_src, n, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(QDR_E_DEVICE, "write_raw: %s", hipGetErrorString(e));
   return ok();

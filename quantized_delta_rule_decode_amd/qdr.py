@@ -50,7 +50,7 @@ class Layout(ctypes.Structure):
 
 
 EXPORTS = ["qdr_pool_bytes", "qdr_pool_create", "qdr_pool_destroy", "qdr_slot_reset",
-           "qdr_pack", "qdr_unpack", "qdr_decode_step", "qdr_get_layout", "qdr_read_raw",
+           "qdr_pack", "qdr_unpack", "qdr_decode_step", "qdr_decode_step_split", "qdr_get_layout", "qdr_read_raw",
            "qdr_write_raw", "qdr_poll_device_error", "qdr_last_error"]
 
 _lib = None
@@ -77,6 +77,7 @@ def load():
         "qdr_pack": [P, P, I32, P, P],
         "qdr_unpack": [P, P, I32, P, P],
         "qdr_decode_step": [P, P, I32, P, P, P, P, P, P, P],
+        "qdr_decode_step_split": [P, P, I32, P, P, P, P, P, P, P, P],
         "qdr_get_layout": [P, ctypes.POINTER(Layout)],
         "qdr_read_raw": [P, I32, P, SZ, P],
         "qdr_write_raw": [P, I32, P, SZ, P],
@@ -205,6 +206,18 @@ class Pool:
             _dptr(q, f32, "q", B * H * DIM), _dptr(k, f32, "k", B * H * DIM),
             _dptr(v, f32, "v", B * H * DIM), _dptr(beta, f32, "beta", B * H),
             _dptr(gate, f32, "gate", gn), _dptr(o, f32, "o", B * H * DIM), _stream(stream)))
+
+    def qdr_decode_step_split(self, slots, q, k, v, beta, gate, o, stream_readout=None, stream_writeback=None):
+        import torch
+        B, H = slots.numel(), self.num_heads
+        f32 = torch.float32
+        gn = B * H if self.gate == GATE_SCALAR else B * H * DIM
+        _check("qdr_decode_step_split", load().qdr_decode_step_split(
+            self._h, _dptr(slots, torch.int32, "slots"), B,
+            _dptr(q, f32, "q", B * H * DIM), _dptr(k, f32, "k", B * H * DIM),
+            _dptr(v, f32, "v", B * H * DIM), _dptr(beta, f32, "beta", B * H),
+            _dptr(gate, f32, "gate", gn), _dptr(o, f32, "o", B * H * DIM),
+            _stream(stream_readout), _stream(stream_writeback)))
 
     def qdr_read_raw(self, slot, stream=None) -> np.ndarray:
         out = np.empty(self.slot_stride, np.uint8)

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(names) == sorted(qdr.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -93,6 +93,7 @@ def test_null_arguments_rejected(lib):
     assert lib.qdr_pool_bytes(None, None) == -1
     assert lib.qdr_pool_destroy(None) == 0
     assert lib.qdr_decode_step(None, None, 0, None, None, None, None, None, None, None) == -1
+    assert lib.qdr_decode_step_split(None, None, 0, None, None, None, None, None, None, None, None) == -1
     assert lib.qdr_pack(None, None, 1, None, None) == -1
     flags = ctypes.c_uint32(0)
     assert lib.qdr_poll_device_error(None, ctypes.byref(flags)) == -1

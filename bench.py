@@ -194,6 +194,20 @@ def two_stream_split(pool, slots, inputs, o, fused_ms: float, reps: int = 5):
             "split_with_work_ms": float(np.mean([r[1] for r in wk]))}
 
 
+def compact_io(cfg, tables, pool, slots, inputs, fused_ms: float, reps: int = 5):
+    """qdr_decode_step_bf16 on the benchmark pool: q, k, v and o in bfloat16
+    (beta, gate fp32); its algorithmic bytes count 2 bytes per q/k/v/o value."""
+    import torch
+    q, k, v, beta, gate = inputs
+    q16, k16, v16 = (x.to(torch.bfloat16) for x in (q, k, v))
+    o16 = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    ms = time_on_stream(lambda: pool.qdr_decode_step_bf16(slots, q16, k16, v16, beta, gate, o16), reps)
+    nbytes = algorithmic_bytes(cfg, tables) - cfg.B * cfg.H * 4 * 128 * 2
+    return {"ms_per_step": ms, "value": cfg.B * cfg.H / (ms * 1e-3), "unit": "state-update steps/s",
+            "algorithmic_bytes_per_step": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "speedup_over_fp32_io": fused_ms / ms}
+
+
 def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
     """HBM rate of a plain in-place streaming kernel on this GPU (torch add_ of
     an fp32 buffer: each byte read once and written once), for scale."""
@@ -217,7 +231,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-comparator", action="store_true",
                     help="skip timing the FP32-state pool of the warm-up")
-    ap.add_argument("--no-split", action="store_true", help="skip timing the two-stream step")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip timing the two-stream step and the bfloat16-I/O step")
     ap.add_argument("--no-trajectory-error", action="store_true",
                     help="skip the quantised-vs-FP32 trajectory error of the small configs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -286,6 +301,7 @@ def main():
     value = head_steps / (gpu_ms * 1e-3)
 
     split = None if args.no_split else two_stream_split(pool, slots, (q, k, v, beta, gate), o, gpu_ms)
+    bf16_io = None if args.no_split else compact_io(cfg, tables, pool, slots, (q, k, v, beta, gate), gpu_ms)
     assert pool.qdr_poll_device_error() == 0
     stream = stream_reference()
     traj = None if args.no_trajectory_error else [fp32_trajectory_error(c) for c in (1, 2, 3)]
@@ -327,6 +343,7 @@ def main():
         "fp32_state_comparator": None if fp32_cmp is None else {
             **fp32_cmp, "speedup_packed_over_fp32": fp32_cmp["ms_per_step"] / gpu_ms},
         "two_stream_split": split,
+        "bf16_io_step": bf16_io,
         "fp32_trajectory_error": traj,
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,

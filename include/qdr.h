@@ -158,6 +158,18 @@ qdr_status qdr_decode_step(qdr_pool *pool, const int32_t *slots, int32_t B,
                            const float *beta, const float *gate, float *o,
                            void *stream);
 
+/* The same step with bfloat16 q, k, v and o (compact I/O: half the bytes of
+ * the fp32 vectors; Review (singularity-lens), compact-bits paragraph, counts
+ * every stored byte).  q, k, v: [B][H][128] bfloat16 (uint16 bit patterns),
+ * widened to fp32 exactly; beta and gate fp32 as in qdr_decode_step; o:
+ * [B][H][128] bfloat16, the fp32 readout rounded to nearest, ties to even.
+ * The state update and the stored state are those of qdr_decode_step on the
+ * widened inputs.  Errors as qdr_decode_step. */
+qdr_status qdr_decode_step_bf16(qdr_pool *pool, const int32_t *slots, int32_t B,
+                                const uint16_t *q, const uint16_t *k,
+                                const uint16_t *v, const float *beta,
+                                const float *gate, uint16_t *o, void *stream);
+
 /* The same step split over two streams (Tutorial §四, engineering paragraph:
  * the head output goes downstream first, and a second stream writes the
  * compressed state back so that the scale update overlaps model compute).

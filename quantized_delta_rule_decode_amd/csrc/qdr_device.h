@@ -341,6 +341,51 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// ---- q, k, v and o: fp32, or bfloat16 in the bfloat16-I/O step mode.
+// A bfloat16 input widens to fp32 exactly; o narrows with round to nearest,
+// ties to even (NaN stays NaN).
+// The step's per-lane inputs: k and q of row `row`, v of columns l and l+64.
+template <bool BF16>
+__device__ __forceinline__ void load_qkv(const LaunchArgs &P, size_t bh, int row, int l, float &kr, float &qr,
+                                         float (&vc)[2]) {
+  const size_t base = bh * kDim;
+  if constexpr (BF16) {
+    const uint16_t *k16 = reinterpret_cast<const uint16_t *>(P.k) + base;
+    const uint16_t *q16 = reinterpret_cast<const uint16_t *>(P.q) + base;
+    const uint16_t *v16 = reinterpret_cast<const uint16_t *>(P.v) + base;
+    const uint32_t a = k16[row], b = q16[row], c = v16[l], d = v16[l + 64];
+    kr = __uint_as_float(a << 16);
+    qr = __uint_as_float(b << 16);
+    vc[0] = __uint_as_float(c << 16);
+    vc[1] = __uint_as_float(d << 16);
+  } else {
+    kr = P.k[base + row];
+    qr = P.q[base + row];
+    vc[0] = P.v[base + l];
+    vc[1] = P.v[base + 64 + l];
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void out_o(const LaunchArgs &P, size_t idx, float x) {
+  if constexpr (BF16) reinterpret_cast<uint16_t *>(P.o)[idx] = bf16_rne(x);
+  else P.o[idx] = x;
+}
+
+// What a mode does: is_step -- the whole step with the store; has_readout --
+// reads q, k, v, beta, gate and writes o; restores -- rebuilds S from codes;
+// io16 -- q, k, v and o in bfloat16.
+constexpr bool is_step(int m) { return m == MODE_STEP || m == MODE_STEP_BF16; }
+constexpr bool has_readout(int m) { return is_step(m) || m == MODE_READOUT; }
+constexpr bool restores(int m) { return has_readout(m) || m == MODE_UNPACK; }
+constexpr bool io16(int m) { return m == MODE_STEP_BF16; }
+
 struct SharedCore {
   float g[kDim];     // restore factor a_i * r_i / q_i (or a_i for float kinds)
   float k[kDim];
@@ -367,6 +412,7 @@ struct Shared : SharedCore {
 // Whole-head kernel: every row of the head has kind BITS.
 // MODE_STEP: restore, gate, delta update, readout, requantise, store.
 // MODE_READOUT: restore, gate, u and delta, readout only (no store).
+// MODE_STEP_BF16: MODE_STEP with bfloat16 q, k, v and o.
 // MODE_PACK: requantise S_in.  MODE_UNPACK: restore into S_out.
 // MODE_RESET: requantise S = 0.
 // --------------------------------------------------------------------------
@@ -402,9 +448,9 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   if (slot < 0 || slot >= P.num_slots) {
     if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
-    if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
-      P.o[bh * kDim + l] = 0.0f;     // wave 0 and 1 cover columns 0..127
-      P.o[bh * kDim + 64 + l] = 0.0f;
+    if (has_readout(MODE) && w == 0 && P.o != nullptr) {
+      out_o<io16(MODE)>(P, bh * kDim + l, 0.0f);     // wave 0 and 1 cover columns 0..127
+      out_o<io16(MODE)>(P, bh * kDim + 64 + l, 0.0f);
     }
     if (MODE == MODE_UNPACK) {
       float *dst = P.S_out + bh * kDim * kDim;
@@ -424,7 +470,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   // ---------------- load codes (both columns of this lane, this wave's rows)
   uint32_t wd[2][K::NW];
-  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
+  if (restores(MODE)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -437,10 +483,10 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   // ---------------- per-row scalars of this lane's row, broadcast via LDS
   float a_row = 1.0f;
-  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
+  if (has_readout(MODE)) {
     a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
   }
-  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
+  if (restores(MODE)) {
     if (INT) {
       const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
       sh.g[row] = (a_row * rn_div(r_row, QMAX)) * GSCALE;
@@ -453,14 +499,12 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     }
   }
   float vcol[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
-    const float kr = (P.k + bh * kDim)[row];
+  if (has_readout(MODE)) {
+    float kr, qr;
+    load_qkv<io16(MODE)>(P, bh, row, l, kr, qr, vcol);
     sh.k[row] = kr;
     sh.b[row] = P.beta[bh] * kr;
-    sh.q[row] = (P.q + bh * kDim)[row];
-    const float *vrow = P.v + bh * kDim;
-    vcol[0] = vrow[l];
-    vcol[1] = vrow[l + 64];
+    sh.q[row] = qr;
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -470,7 +514,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   // wave 0 runs its half of u inside the restore and its q part after the
   // hand-off, wave 1 the other way round.
   float acc1[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP || MODE == MODE_READOUT)
+  if (has_readout(MODE))
     restore_rows<BITS, true, OFF4>(S, acc1, wd, colc, sh.g, (w == 0) ? sh.k : sh.q, 64 * w);
   else if (MODE == MODE_UNPACK)
     restore_rows<BITS, false, OFF4>(S, acc1, wd, colc, sh.g, sh.g, 64 * w);
@@ -501,7 +545,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   // ---------------- delta update
   float oq[2] = {0.0f, 0.0f};
   float dl[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
+  if (has_readout(MODE)) {
     if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
     const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
     if (l == 0) sh.qb[w] = qb_part;
@@ -526,9 +570,8 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       __syncthreads();
       if (w == 0 && P.o != nullptr) {
         const float qb_all = sh.qb[0] + sh.qb[1];
-        float *orow = P.o + bh * kDim;
-        orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
-        orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
+        out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
+        out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
       }
       return;
     }
@@ -591,7 +634,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       sh.cmax[w][l] = fmaxf(cm[0][0], cm[0][1]);
       sh.cmax[w][l + 64] = fmaxf(cm[1][0], cm[1][1]);
     }
-    if (MODE == MODE_STEP && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
+    if (is_step(MODE) && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
     __syncthreads();
     if (SCALE == 0) {
 #pragma unroll
@@ -686,7 +729,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     }
   } else {
     // FP16 / FP32 rows: store the updated values themselves
-    if (MODE == MODE_STEP && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
+    if (is_step(MODE) && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -704,11 +747,10 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   }
 
   // ---------------- the readout
-  if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
+  if (has_readout(MODE) && w == 0 && P.o != nullptr) {
     const float qb_all = sh.qb[0] + sh.qb[1];
-    float *orow = P.o + bh * kDim;
-    orow[l] = (ocol[0] + sh.x[l]) + qb_all * dl[0];
-    orow[l + 64] = (ocol[1] + sh.x[l + 64]) + qb_all * dl[1];
+    out_o<io16(MODE)>(P, bh * kDim + l, (ocol[0] + sh.x[l]) + qb_all * dl[0]);
+    out_o<io16(MODE)>(P, bh * kDim + 64 + l, (ocol[1] + sh.x[l + 64]) + qb_all * dl[1]);
   }
 }
 
@@ -848,10 +890,9 @@ k_rows(const LaunchArgs P) {
 
   if (slot < 0 || slot >= P.num_slots) {
     if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
-    if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
-      float *orow = P.o + bh * kDim;
-      orow[l] = 0.0f;
-      orow[l + 64] = 0.0f;
+    if (has_readout(MODE) && w == 0 && P.o != nullptr) {
+      out_o<io16(MODE)>(P, bh * kDim + l, 0.0f);
+      out_o<io16(MODE)>(P, bh * kDim + 64 + l, 0.0f);
     }
     if (MODE == MODE_UNPACK) {
       float *dst = P.S_out + bh * kDim * kDim;
@@ -879,7 +920,7 @@ k_rows(const LaunchArgs P) {
   float colc[2] = {1.0f, 1.0f};
 
   // ---------------- stage this half's code words in LDS (1 KiB per wave instruction)
-  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
+  if (restores(MODE)) {
     for (uint32_t boff = (uint32_t)l * 16u; boff < half_bytes; boff += 1024u)
       *reinterpret_cast<uint4 *>(codes8 + boff) = load_granule(rs, boff, half_off);
     codes[nwords * kDim + l] = 0u;
@@ -896,8 +937,8 @@ k_rows(const LaunchArgs P) {
   sh.qm[row] = my_q;
   if (FIT) sh.iq[row] = my_int ? rn_div(1.0f, my_q) : 0.0f;
   float a_row = 1.0f;
-  if (MODE == MODE_STEP || MODE == MODE_READOUT) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
-  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
+  if (has_readout(MODE)) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
+  if (restores(MODE)) {
     if (my_int) {
       const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
       sh.g[row] = a_row * rn_div(r_row, my_q);
@@ -910,14 +951,12 @@ k_rows(const LaunchArgs P) {
     }
   }
   float vcol[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
-    const float kr = (P.k + bh * kDim)[row];
+  if (has_readout(MODE)) {
+    float kr, qr;
+    load_qkv<io16(MODE)>(P, bh, row, l, kr, qr, vcol);
     sh.k[row] = kr;
     sh.b[row] = P.beta[bh] * kr;
-    sh.q[row] = (P.q + bh * kDim)[row];
-    const float *vrow = P.v + bh * kDim;
-    vcol[0] = vrow[l];
-    vcol[1] = vrow[l + 64];
+    sh.q[row] = qr;
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -926,7 +965,7 @@ k_rows(const LaunchArgs P) {
   // (u over rows 0..63 in wave 0, the S'^T q part of rows 64..127 in wave 1)
   // in row order.
   float acc1[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP || MODE == MODE_READOUT || MODE == MODE_UNPACK) {
+  if (restores(MODE)) {
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 g4 = lds4(&sh.g[64 * w + 4 * i4]);
@@ -959,7 +998,7 @@ k_rows(const LaunchArgs P) {
         }
       }
     }
-    if (MODE == MODE_STEP || MODE == MODE_READOUT) chain_rows(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
+    if (has_readout(MODE)) chain_rows(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
   }
 
   if (MODE == MODE_UNPACK) {
@@ -987,7 +1026,7 @@ k_rows(const LaunchArgs P) {
   // ---------------- delta update (same hand-off as k_head)
   float oq[2] = {0.0f, 0.0f};
   float dl[2] = {0.0f, 0.0f};
-  if (MODE == MODE_STEP || MODE == MODE_READOUT) {
+  if (has_readout(MODE)) {
     if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
     const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
     if (l == 0) sh.qb[w] = qb_part;
@@ -1012,9 +1051,8 @@ k_rows(const LaunchArgs P) {
       __syncthreads();
       if (w == 0 && P.o != nullptr) {
         const float qb_all = sh.qb[0] + sh.qb[1];
-        float *orow = P.o + bh * kDim;
-        orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
-        orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
+        out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
+        out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
       }
       return;
     }
@@ -1078,7 +1116,7 @@ k_rows(const LaunchArgs P) {
     sh.cmax[w][l] = cm[0];
     sh.cmax[w][l + 64] = cm[1];
   }
-  if (MODE == MODE_STEP && w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
+  if (is_step(MODE) && w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
   __syncthreads();
   if (SCALE == 0) {
 #pragma unroll
@@ -1225,11 +1263,10 @@ k_rows(const LaunchArgs P) {
   }
 
   // ---------------- readout
-  if ((MODE == MODE_STEP || MODE == MODE_READOUT) && w == 0 && P.o != nullptr) {
+  if (has_readout(MODE) && w == 0 && P.o != nullptr) {
     const float qb_all = sh.qb[0] + sh.qb[1];
-    float *orow = P.o + bh * kDim;
-    orow[l] = (oq[0] + sh.x[l]) + qb_all * dl[0];
-    orow[l + 64] = (oq[1] + sh.x[l + 64]) + qb_all * dl[1];
+    out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
+    out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
   }
 }
 
@@ -1287,6 +1324,7 @@ hipError_t launch_head_modes(const PoolConfig &cfg, const LaunchArgs &a, int n, 
   switch (mode) {
     case MODE_STEP: return launch_head_kind<BITS, MODE_STEP>(cfg, a, n, st);
     case MODE_READOUT: return launch_head_kind<BITS, MODE_READOUT>(cfg, a, n, st);
+    case MODE_STEP_BF16: return launch_head_kind<BITS, MODE_STEP_BF16>(cfg, a, n, st);
     case MODE_PACK: return launch_head_kind<BITS, MODE_PACK>(cfg, a, n, st);
     case MODE_UNPACK: return launch_head_kind<BITS, MODE_UNPACK>(cfg, a, n, st);
     default: return launch_head_kind<BITS, MODE_RESET>(cfg, a, n, st);

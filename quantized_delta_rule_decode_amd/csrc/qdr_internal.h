@@ -11,7 +11,7 @@ namespace qdr {
 
 constexpr int kDim = 128;
 
-enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3, MODE_READOUT = 4 };
+enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3, MODE_READOUT = 4, MODE_STEP_BF16 = 5 };
 
 // Per-head metadata on the device (16 bytes).
 struct HeadInfo {
@@ -62,8 +62,8 @@ struct LaunchArgs {
   const float *omega;         // [H*128]
   uint32_t *err;              // device error word
   const int32_t *slots;       // [n] slot of each request / dense entry
-  const float *q, *k, *v, *beta, *gate;
-  float *o;
+  const float *q, *k, *v, *beta, *gate;   // q, k, v: uint16 bfloat16 data in MODE_STEP_BF16
+  float *o;                               // uint16 bfloat16 data in MODE_STEP_BF16
   const float *S_in;          // pack: [n][H][128][128]
   float *S_out;               // unpack
 };
@@ -83,6 +83,7 @@ hipError_t launch_head_int_pack(const PoolConfig &, const LaunchArgs &, int n, h
 hipError_t launch_head_int_unpack(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_int_reset(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_int_readout(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
+hipError_t launch_head_int_step_bf16(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_b16(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 hipError_t launch_head_b32(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 // Row-unit launch (qdr_rows.hip) over the heads in list[0..count).

@@ -420,6 +420,28 @@ qdr_status qdr_decode_step(qdr_pool *pool, const int32_t *slots, int32_t B, cons
   return dispatch(pool, a, B, qdr::MODE_STEP, st);
 }
 
+qdr_status qdr_decode_step_bf16(qdr_pool *pool, const int32_t *slots, int32_t B, const uint16_t *q,
+                                const uint16_t *k, const uint16_t *v, const float *beta, const float *gate,
+                                uint16_t *o, void *stream) {
+  if (!pool) return fail(QDR_E_INVAL, "pool is NULL");
+  if (B < 0) return fail(QDR_E_INVAL, "B must be >= 0");
+  if (B == 0) return ok();
+  if (!slots || !q || !k || !v || !beta || !gate || !o)
+    return fail(QDR_E_INVAL, "a tensor pointer is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  qdr_status cs = check_slots_host(pool, slots, B, st, true);
+  if (cs != QDR_OK) return cs;
+  qdr::LaunchArgs a = base_args(pool);
+  a.slots = slots;
+  a.q = reinterpret_cast<const float *>(q);
+  a.k = reinterpret_cast<const float *>(k);
+  a.v = reinterpret_cast<const float *>(v);
+  a.beta = beta;
+  a.gate = gate;
+  a.o = reinterpret_cast<float *>(o);
+  return dispatch(pool, a, B, qdr::MODE_STEP_BF16, st);
+}
+
 qdr_status qdr_decode_step_split(qdr_pool *pool, const int32_t *slots, int32_t B, const float *q, const float *k,
                                  const float *v, const float *beta, const float *gate, float *o,
                                  void *stream_readout, void *stream_writeback) {

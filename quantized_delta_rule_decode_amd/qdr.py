@@ -50,7 +50,7 @@ class Layout(ctypes.Structure):
 
 
 EXPORTS = ["qdr_pool_bytes", "qdr_pool_create", "qdr_pool_destroy", "qdr_slot_reset",
-           "qdr_pack", "qdr_unpack", "qdr_decode_step", "qdr_decode_step_split", "qdr_get_layout", "qdr_read_raw",
+           "qdr_pack", "qdr_unpack", "qdr_decode_step", "qdr_decode_step_split", "qdr_decode_step_bf16", "qdr_get_layout", "qdr_read_raw",
            "qdr_write_raw", "qdr_poll_device_error", "qdr_last_error"]
 
 _lib = None
@@ -78,6 +78,7 @@ def load():
         "qdr_unpack": [P, P, I32, P, P],
         "qdr_decode_step": [P, P, I32, P, P, P, P, P, P, P],
         "qdr_decode_step_split": [P, P, I32, P, P, P, P, P, P, P, P],
+        "qdr_decode_step_bf16": [P, P, I32, P, P, P, P, P, P, P],
         "qdr_get_layout": [P, ctypes.POINTER(Layout)],
         "qdr_read_raw": [P, I32, P, SZ, P],
         "qdr_write_raw": [P, I32, P, SZ, P],
@@ -206,6 +207,18 @@ class Pool:
             _dptr(q, f32, "q", B * H * DIM), _dptr(k, f32, "k", B * H * DIM),
             _dptr(v, f32, "v", B * H * DIM), _dptr(beta, f32, "beta", B * H),
             _dptr(gate, f32, "gate", gn), _dptr(o, f32, "o", B * H * DIM), _stream(stream)))
+
+    def qdr_decode_step_bf16(self, slots, q, k, v, beta, gate, o, stream=None):
+        """q, k, v, o: torch.bfloat16 [B][H][128]; beta, gate fp32."""
+        import torch
+        B, H = slots.numel(), self.num_heads
+        bf, f32 = torch.bfloat16, torch.float32
+        gn = B * H if self.gate == GATE_SCALAR else B * H * DIM
+        _check("qdr_decode_step_bf16", load().qdr_decode_step_bf16(
+            self._h, _dptr(slots, torch.int32, "slots"), B,
+            _dptr(q, bf, "q", B * H * DIM), _dptr(k, bf, "k", B * H * DIM),
+            _dptr(v, bf, "v", B * H * DIM), _dptr(beta, f32, "beta", B * H),
+            _dptr(gate, f32, "gate", gn), _dptr(o, bf, "o", B * H * DIM), _stream(stream)))
 
     def qdr_decode_step_split(self, slots, q, k, v, beta, gate, o, stream_readout=None, stream_writeback=None):
         import torch

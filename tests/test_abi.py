@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "qdr.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qdr_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qdr_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(names) == sorted(qdr.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -94,6 +94,7 @@ def test_null_arguments_rejected(lib):
     assert lib.qdr_pool_destroy(None) == 0
     assert lib.qdr_decode_step(None, None, 0, None, None, None, None, None, None, None) == -1
     assert lib.qdr_decode_step_split(None, None, 0, None, None, None, None, None, None, None, None) == -1
+    assert lib.qdr_decode_step_bf16(None, None, 0, None, None, None, None, None, None, None) == -1
     assert lib.qdr_pack(None, None, 1, None, None) == -1
     flags = ctypes.c_uint32(0)
     assert lib.qdr_poll_device_error(None, ctypes.byref(flags)) == -1

@@ -25,7 +25,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 SOURCES = ["qdr_head_int_step.hip", "qdr_head_int_pack.hip", "qdr_head_int_unpack.hip",
-           "qdr_head_int_reset.hip", "qdr_head_int_readout.hip", "qdr_head_int_step_bf16.hip", "qdr_head_fp16.hip", "qdr_head_fp32.hip", "qdr_rows.hip", "qdr_dispatch.cpp",
+           "qdr_head_int_reset.hip", "qdr_head_int_readout.hip", "qdr_head_int_step_bf16.hip", "qdr_head_int_writeback.hip", "qdr_head_fp16.hip", "qdr_head_fp32.hip", "qdr_rows.hip", "qdr_dispatch.cpp",
            "qdr_runtime.cpp"]
 # every file the device code is built from (a change to any of them changes the kernels)
 DEVICE_SOURCES = ["qdr_device.h", "qdr_internal.h"] + [s for s in SOURCES if s.endswith(".hip")]

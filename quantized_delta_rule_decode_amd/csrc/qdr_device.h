@@ -379,11 +379,12 @@ __device__ __forceinline__ void out_o(const LaunchArgs &P, size_t idx, float x) 
 }
 
 // What a mode does: is_step -- the whole step with the store; has_readout --
-// reads q, k, v, beta, gate and writes o; restores -- rebuilds S from codes;
-// io16 -- q, k, v and o in bfloat16.
-constexpr bool is_step(int m) { return m == MODE_STEP || m == MODE_STEP_BF16; }
+// reads q, k, v, beta, gate and computes the readout; writes_o -- stores it;
+// restores -- rebuilds S from codes; io16 -- q, k, v and o in bfloat16.
+constexpr bool is_step(int m) { return m == MODE_STEP || m == MODE_STEP_BF16 || m == MODE_WRITEBACK; }
 constexpr bool has_readout(int m) { return is_step(m) || m == MODE_READOUT; }
 constexpr bool restores(int m) { return has_readout(m) || m == MODE_UNPACK; }
+constexpr bool writes_o(int m) { return has_readout(m) && m != MODE_WRITEBACK; }
 constexpr bool io16(int m) { return m == MODE_STEP_BF16; }
 
 struct SharedCore {
@@ -413,6 +414,8 @@ struct Shared : SharedCore {
 // MODE_STEP: restore, gate, delta update, readout, requantise, store.
 // MODE_READOUT: restore, gate, u and delta, readout only (no store).
 // MODE_STEP_BF16: MODE_STEP with bfloat16 q, k, v and o.
+// MODE_WRITEBACK: MODE_STEP without the o store (the second half of the
+// two-stream step).
 // MODE_PACK: requantise S_in.  MODE_UNPACK: restore into S_out.
 // MODE_RESET: requantise S = 0.
 // --------------------------------------------------------------------------
@@ -448,7 +451,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   if (slot < 0 || slot >= P.num_slots) {
     if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
-    if (has_readout(MODE) && w == 0 && P.o != nullptr) {
+    if (writes_o(MODE) && w == 0 && P.o != nullptr) {
       out_o<io16(MODE)>(P, bh * kDim + l, 0.0f);     // wave 0 and 1 cover columns 0..127
       out_o<io16(MODE)>(P, bh * kDim + 64 + l, 0.0f);
     }
@@ -747,7 +750,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   }
 
   // ---------------- the readout
-  if (has_readout(MODE) && w == 0 && P.o != nullptr) {
+  if (writes_o(MODE) && w == 0 && P.o != nullptr) {
     const float qb_all = sh.qb[0] + sh.qb[1];
     out_o<io16(MODE)>(P, bh * kDim + l, (ocol[0] + sh.x[l]) + qb_all * dl[0]);
     out_o<io16(MODE)>(P, bh * kDim + 64 + l, (ocol[1] + sh.x[l + 64]) + qb_all * dl[1]);
@@ -890,7 +893,7 @@ k_rows(const LaunchArgs P) {
 
   if (slot < 0 || slot >= P.num_slots) {
     if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
-    if (has_readout(MODE) && w == 0 && P.o != nullptr) {
+    if (writes_o(MODE) && w == 0 && P.o != nullptr) {
       out_o<io16(MODE)>(P, bh * kDim + l, 0.0f);
       out_o<io16(MODE)>(P, bh * kDim + 64 + l, 0.0f);
     }
@@ -1263,7 +1266,7 @@ k_rows(const LaunchArgs P) {
   }
 
   // ---------------- readout
-  if (has_readout(MODE) && w == 0 && P.o != nullptr) {
+  if (writes_o(MODE) && w == 0 && P.o != nullptr) {
     const float qb_all = sh.qb[0] + sh.qb[1];
     out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
     out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
@@ -1325,6 +1328,7 @@ hipError_t launch_head_modes(const PoolConfig &cfg, const LaunchArgs &a, int n, 
     case MODE_STEP: return launch_head_kind<BITS, MODE_STEP>(cfg, a, n, st);
     case MODE_READOUT: return launch_head_kind<BITS, MODE_READOUT>(cfg, a, n, st);
     case MODE_STEP_BF16: return launch_head_kind<BITS, MODE_STEP_BF16>(cfg, a, n, st);
+    case MODE_WRITEBACK: return launch_head_kind<BITS, MODE_WRITEBACK>(cfg, a, n, st);
     case MODE_PACK: return launch_head_kind<BITS, MODE_PACK>(cfg, a, n, st);
     case MODE_UNPACK: return launch_head_kind<BITS, MODE_UNPACK>(cfg, a, n, st);
     default: return launch_head_kind<BITS, MODE_RESET>(cfg, a, n, st);

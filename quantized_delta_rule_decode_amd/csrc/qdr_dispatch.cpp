@@ -17,6 +17,7 @@ hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const ListE
       case MODE_STEP: e = launch_head_int_step(cfg, args, n, stream); break;
       case MODE_READOUT: e = launch_head_int_readout(cfg, args, n, stream); break;
       case MODE_STEP_BF16: e = launch_head_int_step_bf16(cfg, args, n, stream); break;
+      case MODE_WRITEBACK: e = launch_head_int_writeback(cfg, args, n, stream); break;
       case MODE_PACK: e = launch_head_int_pack(cfg, args, n, stream); break;
       case MODE_UNPACK: e = launch_head_int_unpack(cfg, args, n, stream); break;
       default: e = launch_head_int_reset(cfg, args, n, stream); break;

@@ -11,7 +11,8 @@ namespace qdr {
 
 constexpr int kDim = 128;
 
-enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3, MODE_READOUT = 4, MODE_STEP_BF16 = 5 };
+enum Mode : int { MODE_STEP = 0, MODE_PACK = 1, MODE_UNPACK = 2, MODE_RESET = 3, MODE_READOUT = 4, MODE_STEP_BF16 = 5,
+                  MODE_WRITEBACK = 6 };
 
 // Per-head metadata on the device (16 bytes).
 struct HeadInfo {
@@ -84,6 +85,7 @@ hipError_t launch_head_int_unpack(const PoolConfig &, const LaunchArgs &, int n,
 hipError_t launch_head_int_reset(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_int_readout(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_int_step_bf16(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
+hipError_t launch_head_int_writeback(const PoolConfig &, const LaunchArgs &, int n, hipStream_t);
 hipError_t launch_head_b16(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 hipError_t launch_head_b32(const PoolConfig &, const LaunchArgs &, int n, int mode, hipStream_t);
 // Row-unit launch (qdr_rows.hip) over the heads in list[0..count).

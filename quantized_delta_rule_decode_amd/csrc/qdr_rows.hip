@@ -52,6 +52,7 @@ hipError_t launch_rows_mode(const PoolConfig &cfg, const LaunchArgs &a, int n, c
     case MODE_STEP: return launch_rows<MODE_STEP>(cfg, a, n, list, count, st);
     case MODE_READOUT: return launch_rows<MODE_READOUT>(cfg, a, n, list, count, st);
     case MODE_STEP_BF16: return launch_rows<MODE_STEP_BF16>(cfg, a, n, list, count, st);
+    case MODE_WRITEBACK: return launch_rows<MODE_WRITEBACK>(cfg, a, n, list, count, st);
     case MODE_PACK: return launch_rows<MODE_PACK>(cfg, a, n, list, count, st);
     case MODE_UNPACK: return launch_rows<MODE_UNPACK>(cfg, a, n, list, count, st);
     default: return launch_rows<MODE_RESET>(cfg, a, n, list, count, st);

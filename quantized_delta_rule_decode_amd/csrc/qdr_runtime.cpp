@@ -478,7 +478,7 @@ qdr_status qdr_decode_step_split(qdr_pool *pool, const int32_t *slots, int32_t B
   if (e == hipSuccess) e = hipStreamWaitEvent(sw, pool->wb_done, 0);
   if (e != hipSuccess) return fail(QDR_E_DEVICE, "stream ordering failed: %s", hipGetErrorString(e));
   a.o = nullptr;
-  st = dispatch(pool, a, B, qdr::MODE_STEP, sw);
+  st = dispatch(pool, a, B, qdr::MODE_WRITEBACK, sw);
   if (st != QDR_OK) return st;
   // 3. later calls on this pool, on any stream, wait for the write-back
   e = hipEventRecord(pool->wb_done, sw);

@@ -29,16 +29,17 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "state-update steps/s (requests x heads) at B=512, 6-bit; achieved HBM GB/s"
 
 
-def algorithmic_bytes(cfg, tables) -> int:
+def algorithmic_bytes(cfg, tables, scale_bits: int = 32) -> int:
     """Bytes one step must move by the method's own accounting: every code
     (b bits per state value of its row, no layout padding) and every scale
-    read and written once, q/k/v, beta and the gate read, o written."""
+    (scale_bits wide) read and written once, q/k/v, beta and the gate read,
+    o written."""
     H = cfg.H
     kinds = np.asarray(tables["kinds"], np.int64)
     rows = np.repeat(kinds, 128).reshape(H, 128) if cfg.unit == 0 else kinds.reshape(H, 128)
     code = rows.sum(axis=1) * 128 // 8                       # bytes per head
     has_int = (rows <= 8).any(axis=1)
-    scales = np.where(has_int, (2 if cfg.scale_mode == 0 else 1) * 128 * 4, 0)
+    scales = np.where(has_int, (2 if cfg.scale_mode == 0 else 1) * 128 * scale_bits // 8, 0)
     gate_bytes = 4 if cfg.gate == 0 else 4 * 128
     per_req = int((2 * code + 2 * scales).sum()) + H * (3 * 128 * 4 + 4 + gate_bytes + 128 * 4)
     return per_req * cfg.B
@@ -208,6 +209,32 @@ def compact_io(cfg, tables, pool, slots, inputs, fused_ms: float, reps: int = 5)
             "speedup_over_fp32_io": fused_ms / ms}
 
 
+def compact_scales(cfg, tables, pool, slots, inputs, o, fused_ms: float, reps: int = 5, chunk: int = 16):
+    """The step on a pool that stores its scale factors as bfloat16: the
+    benchmark pool's state is restored chunk by chunk (qdr_unpack) and packed
+    into a 16-bit-scale pool of the same layout otherwise, then that pool's
+    qdr_decode_step is timed on the same inputs."""
+    import torch
+    from quantized_delta_rule_decode_amd import qdr, workload
+    p16 = workload.make_pool(cfg, tables, scale_bits=16)
+    S = torch.empty((min(chunk, cfg.B), cfg.H, qdr.DIM, qdr.DIM), dtype=torch.float32, device=o.device)
+    for i in range(0, cfg.B, chunk):
+        s = slots[i:i + chunk]
+        pool.qdr_unpack(s, S[:s.numel()])
+        p16.qdr_pack(s, S[:s.numel()])
+    del S
+    torch.cuda.synchronize()
+    ms = time_on_stream(lambda: p16.qdr_decode_step(slots, *inputs, o), reps)
+    assert p16.qdr_poll_device_error() == 0
+    nbytes = algorithmic_bytes(cfg, tables, scale_bits=16)
+    out = {"ms_per_step": ms, "value": cfg.B * cfg.H / (ms * 1e-3), "unit": "state-update steps/s",
+           "stored_bits_per_value": round(p16.bits_per_value, 3), "pool_bytes": p16.total_bytes,
+           "algorithmic_bytes_per_step": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+           "speedup_over_fp32_scales": fused_ms / ms}
+    p16.close()
+    return out
+
+
 def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
     """HBM rate of a plain in-place streaming kernel on this GPU (torch add_ of
     an fp32 buffer: each byte read once and written once), for scale."""
@@ -232,7 +259,8 @@ def main():
     ap.add_argument("--no-fp32-comparator", action="store_true",
                     help="skip timing the FP32-state pool of the warm-up")
     ap.add_argument("--no-split", action="store_true",
-                    help="skip timing the two-stream step and the bfloat16-I/O step")
+                    help="skip timing the two-stream step, the bfloat16-I/O step and the "
+                         "bfloat16-scale pool")
     ap.add_argument("--no-trajectory-error", action="store_true",
                     help="skip the quantised-vs-FP32 trajectory error of the small configs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -302,6 +330,7 @@ def main():
 
     split = None if args.no_split else two_stream_split(pool, slots, (q, k, v, beta, gate), o, gpu_ms)
     bf16_io = None if args.no_split else compact_io(cfg, tables, pool, slots, (q, k, v, beta, gate), gpu_ms)
+    sc16 = None if args.no_split else compact_scales(cfg, tables, pool, slots, (q, k, v, beta, gate), o, gpu_ms)
     assert pool.qdr_poll_device_error() == 0
     stream = stream_reference()
     traj = None if args.no_trajectory_error else [fp32_trajectory_error(c) for c in (1, 2, 3)]
@@ -344,6 +373,7 @@ def main():
             **fp32_cmp, "speedup_packed_over_fp32": fp32_cmp["ms_per_step"] / gpu_ms},
         "two_stream_split": split,
         "bf16_io_step": bf16_io,
+        "bf16_scales_step": sc16,
         "fp32_trajectory_error": traj,
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,

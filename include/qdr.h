@@ -94,6 +94,14 @@ typedef struct {
   const float *omega;     /* HOST: [num_heads*128] row-impact weights,
                              finite, in [2^-40, 2^40]; ignored for
                              ROW_ABSMAX (may be NULL); copied                */
+  int32_t scale_bits;     /* stored width of the factors r and c: 0 or 32 =
+                             fp32; 16 = bfloat16 (compact storage; Review-SL,
+                             compact-bits paragraph).  With 16 the row factor
+                             and the clip-free column factor are rounded up to
+                             bfloat16 before the codes are computed from
+                             them, a refitted column factor is rounded to
+                             nearest even, and the restore reads the stored
+                             values                                           */
 } qdr_pool_desc;
 
 typedef struct {

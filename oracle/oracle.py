@@ -57,7 +57,7 @@ class PoolDesc(ctypes.Structure):
     _fields_ = [("num_slots", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("unit", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("scale_mode", ctypes.c_int32), ("fit_iters", ctypes.c_int32),
-                ("kinds", _p), ("omega", _p)]
+                ("kinds", _p), ("omega", _p), ("scale_bits", ctypes.c_int32)]
 
 
 def _declare(L):
@@ -70,16 +70,20 @@ def _declare(L):
     L.or_dequant.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _p]
     L.or_delta_update.argtypes = [ctypes.c_int, _p, _p, _p, ctypes.c_float, _p, _p]
     L.or_readout.argtypes = [ctypes.c_int, _p, _p, _p]
-    L.or_requant.argtypes = [ctypes.c_int, _p, _p, _p, ctypes.c_int, ctypes.c_int,
+    L.or_requant.argtypes = [ctypes.c_int, _p, _p, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                              _p, _p, _p, _p]
     L.or_head_step.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, ctypes.c_int,
-                               ctypes.c_int, _p, _p, _p, ctypes.c_float, _p, _p, _p]
+                               ctypes.c_int, ctypes.c_int, _p, _p, _p, ctypes.c_float, _p, _p, _p]
+    L.or_bf16_up.restype = ctypes.c_float
+    L.or_bf16_up.argtypes = [ctypes.c_float]
+    L.or_bf16_nearest.restype = ctypes.c_float
+    L.or_bf16_nearest.argtypes = [ctypes.c_float]
     L.or_block_bytes.restype = ctypes.c_size_t
-    L.or_block_bytes.argtypes = [_p, ctypes.c_int, ctypes.c_int]
+    L.or_block_bytes.argtypes = [_p, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.or_code_bytes.restype = ctypes.c_size_t
     L.or_code_bytes.argtypes = [_p, ctypes.c_int]
-    L.or_encode_block.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p]
-    L.or_decode_block.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p]
+    L.or_encode_block.argtypes = [_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p]
+    L.or_decode_block.argtypes = [_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p]
     L.or_pool_layout.argtypes = [ctypes.POINTER(PoolDesc), _p, _p, _p]
     L.or_pool_step.restype = ctypes.c_int
     L.or_pool_step.argtypes = [ctypes.POINTER(PoolDesc), _p, _p, ctypes.c_int32,
@@ -108,6 +112,14 @@ def f32_to_f16(x: float) -> int:
 
 def f16_to_f32(h: int) -> float:
     return float(lib().or_f16_to_f32(ctypes.c_uint16(h)))
+
+
+def bf16_up(x: float) -> float:
+    return float(lib().or_bf16_up(ctypes.c_float(x)))
+
+
+def bf16_nearest(x: float) -> float:
+    return float(lib().or_bf16_nearest(ctypes.c_float(x)))
 
 
 def fold_sum(x) -> float:
@@ -145,7 +157,7 @@ def readout(S, q):
     return o
 
 
-def requant(kinds, S, omega, scale_mode=SCALE_DUAL, fit_iters=0):
+def requant(kinds, S, omega, scale_mode=SCALE_DUAL, fit_iters=0, scale_bits=32):
     kinds = _c(kinds, np.uint8)
     d = kinds.size
     S = _c(S, np.float32)
@@ -154,12 +166,12 @@ def requant(kinds, S, omega, scale_mode=SCALE_DUAL, fit_iters=0):
     r = np.empty(d, np.float32)
     c = np.empty(d, np.float32)
     m = np.empty(d, np.float32)
-    lib().or_requant(d, _ptr(kinds), _ptr(S), _ptr(omega), scale_mode, fit_iters,
+    lib().or_requant(d, _ptr(kinds), _ptr(S), _ptr(omega), scale_mode, fit_iters, scale_bits,
                      _ptr(e), _ptr(r), _ptr(c), _ptr(m))
     return e, r, c, m
 
 
-def head_step(kinds, e, r, c, omega, q, k, v, beta, a, scale_mode=SCALE_DUAL, fit_iters=0):
+def head_step(kinds, e, r, c, omega, q, k, v, beta, a, scale_mode=SCALE_DUAL, fit_iters=0, scale_bits=32):
     """Returns (e', r', c', o, S_pre) without modifying the inputs."""
     kinds = _c(kinds, np.uint8)
     d = kinds.size
@@ -170,7 +182,7 @@ def head_step(kinds, e, r, c, omega, q, k, v, beta, a, scale_mode=SCALE_DUAL, fi
     o = np.empty(d, np.float32)
     S_pre = np.empty((d, d), np.float32)
     lib().or_head_step(d, _ptr(kinds), _ptr(e), _ptr(r), _ptr(c), _ptr(omega), scale_mode,
-                       fit_iters, _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(beta), _ptr(a),
+                       fit_iters, scale_bits, _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(beta), _ptr(a),
                        _ptr(o), _ptr(S_pre))
     return e, r, c, o, S_pre
 
@@ -181,9 +193,9 @@ def codes_signed(e, kinds):
 
 
 # ---------------------------------------------------------------- blocks
-def block_bytes(kinds, unit, scale_mode):
+def block_bytes(kinds, unit, scale_mode, scale_bits=32):
     kinds = _c(kinds, np.uint8)
-    return int(lib().or_block_bytes(_ptr(kinds), unit, scale_mode))
+    return int(lib().or_block_bytes(_ptr(kinds), unit, scale_mode, scale_bits))
 
 
 def code_bytes(kinds, unit):
@@ -191,21 +203,21 @@ def code_bytes(kinds, unit):
     return int(lib().or_code_bytes(_ptr(kinds), unit))
 
 
-def encode_block(kinds, unit, scale_mode, e, r, c):
+def encode_block(kinds, unit, scale_mode, e, r, c, scale_bits=32):
     kinds = _c(kinds, np.uint8)
     e, r, c = _c(e, np.uint32), _c(r, np.float32), _c(c, np.float32)
-    out = np.zeros(block_bytes(kinds, unit, scale_mode), np.uint8)
-    lib().or_encode_block(_ptr(kinds), unit, scale_mode, _ptr(e), _ptr(r), _ptr(c), _ptr(out))
+    out = np.zeros(block_bytes(kinds, unit, scale_mode, scale_bits), np.uint8)
+    lib().or_encode_block(_ptr(kinds), unit, scale_mode, scale_bits, _ptr(e), _ptr(r), _ptr(c), _ptr(out))
     return out
 
 
-def decode_block(kinds, unit, scale_mode, block):
+def decode_block(kinds, unit, scale_mode, block, scale_bits=32):
     kinds = _c(kinds, np.uint8)
     block = _c(block, np.uint8)
     e = np.zeros((128, 128), np.uint32)
     r = np.empty(128, np.float32)
     c = np.empty(128, np.float32)
-    lib().or_decode_block(_ptr(kinds), unit, scale_mode, _ptr(block), _ptr(e), _ptr(r), _ptr(c))
+    lib().or_decode_block(_ptr(kinds), unit, scale_mode, scale_bits, _ptr(block), _ptr(e), _ptr(r), _ptr(c))
     return e, r, c
 
 
@@ -214,11 +226,12 @@ class Pool:
     """Host image of a state pool in the oracle's own layout."""
 
     def __init__(self, num_slots, num_heads, kinds, omega, unit=UNIT_HEAD,
-                 gate=GATE_SCALAR, scale_mode=SCALE_DUAL, fit_iters=0):
+                 gate=GATE_SCALAR, scale_mode=SCALE_DUAL, fit_iters=0, scale_bits=32):
         self.kinds = _c(kinds, np.uint8)
         self.omega = _c(omega, np.float32)
+        self.scale_bits = scale_bits
         self.desc = PoolDesc(num_slots, num_heads, unit, gate, scale_mode, fit_iters,
-                             _ptr(self.kinds).value, _ptr(self.omega).value)
+                             _ptr(self.kinds).value, _ptr(self.omega).value, scale_bits)
         H = num_heads
         self.head_off = np.zeros(H, np.uint64)
         stride = ctypes.c_uint64(0)
@@ -241,7 +254,7 @@ class Pool:
         return self.kinds[h * 128:(h + 1) * 128]
 
     def block_size(self, h):
-        return block_bytes(self.head_kinds(h), self.unit, self.scale_mode)
+        return block_bytes(self.head_kinds(h), self.unit, self.scale_mode, self.scale_bits)
 
     def block_view(self, slot, h):
         off = slot * self.slot_stride + int(self.head_off[h])

@@ -190,9 +190,35 @@ void or_readout(int d, const float *S, const float *q, float *o) {
  * FP16 rows: binary16 of S.  FP32 rows: S itself.
  * Non-integer rows take no part in r or c; their r_i is stored as 0.
  */
+/* ---- bfloat16 factors (compact scale storage, the compact-bits paragraph
+ * of [SLR] counts 16-bit factors).  A bfloat16 value is a binary32 value
+ * whose low 16 bits are zero.  Reading taken: the row factor and the
+ * clip-free column factor are rounded UP before the codes are computed from
+ * them (so |Y| <= 1 still holds and no code leaves +-q), a refitted column
+ * factor is rounded to nearest; the restore uses the stored values. */
+static float bf16_toward_zero(float x) { return u2f(f2u(x) & 0xFFFF0000u); }
+static float bf16_away(float t) { return u2f(f2u(t) + 0x10000u); }  /* next bfloat16 away from 0 */
+
+float or_bf16_up(float x) {
+  float t = bf16_toward_zero(x);
+  return (t < x) ? bf16_away(t) : t;
+}
+
+float or_bf16_nearest(float x) {
+  float lo = bf16_toward_zero(x);
+  if (lo == x) return x;
+  float hi = bf16_away(lo);
+  double dl = fabs((double)x - (double)lo), dh = fabs((double)hi - (double)x);
+  if (dl < dh) return lo;
+  if (dh < dl) return hi;
+  return (f2u(lo) & 0x10000u) ? hi : lo;
+}
+
 void or_requant(int d, const uint8_t *kinds, const float *S,
                 const float *omega, int scale_mode, int fit_iters,
-                uint32_t *e, float *r, float *c, float *m_out) {
+                int scale_bits, uint32_t *e, float *r, float *c,
+                float *m_out) {
+  const int b16 = scale_bits == 16;
   float *tmp = (float *)malloc(sizeof(float) * (size_t)d);
   float *ir = (float *)malloc(sizeof(float) * (size_t)d);
   float *m = (float *)malloc(sizeof(float) * (size_t)d);
@@ -223,6 +249,7 @@ void or_requant(int d, const uint8_t *kinds, const float *S,
       for (int j = 0; j < d; ++j) mx = fmaxf(mx, fabsf(S[i * d + j]));
       r[i] = (mx < FLT_MIN) ? 1.0f : mx;
     }
+    if (b16) r[i] = or_bf16_up(r[i]);
     ir[i] = 1.0f / r[i];
   }
 
@@ -234,6 +261,7 @@ void or_requant(int d, const uint8_t *kinds, const float *S,
       for (int i = 0; i < d; ++i)
         if (kind_is_int(kinds[i])) mx = fmaxf(mx, fabsf(S[i * d + j] * ir[i]));
       c0 = (mx < FLT_MIN) ? 1.0f : mx;
+      if (b16) c0 = or_bf16_up(c0);
     }
     float ec = 1.0f / c0;
     float num = 0.0f, den = 0.0f;
@@ -253,6 +281,7 @@ void or_requant(int d, const uint8_t *kinds, const float *S,
       }
     }
     c[j] = (fit_iters > 0 && den > 0.0f) ? num / den : c0;
+    if (b16 && fit_iters > 0) c[j] = or_bf16_nearest(c[j]);
   }
   if (m_out) memcpy(m_out, m, sizeof(float) * (size_t)d);
   free(tmp);
@@ -268,7 +297,7 @@ void or_requant(int d, const uint8_t *kinds, const float *S,
 /* ------------------------------------------------------------------------ */
 void or_head_step(int d, const uint8_t *kinds, uint32_t *e, float *r,
                   float *c, const float *omega, int scale_mode,
-                  int fit_iters, const float *q, const float *k,
+                  int fit_iters, int scale_bits, const float *q, const float *k,
                   const float *v, float beta, const float *a, float *o,
                   float *S_pre) {
   size_t nn = (size_t)d * (size_t)d;
@@ -278,7 +307,7 @@ void or_head_step(int d, const uint8_t *kinds, uint32_t *e, float *r,
   or_delta_update(d, Sp, k, v, beta, S, NULL);
   or_readout(d, S, q, o);
   if (S_pre) memcpy(S_pre, S, sizeof(float) * nn);
-  or_requant(d, kinds, S, omega, scale_mode, fit_iters, e, r, c, NULL);
+  or_requant(d, kinds, S, omega, scale_mode, fit_iters, scale_bits, e, r, c, NULL);
   free(Sp);
   free(S);
 }
@@ -332,13 +361,15 @@ size_t or_code_bytes(const uint8_t *kinds, int unit) {
   return ng * D128 * (size_t)granule_bytes(unit);
 }
 
-static size_t scale_bytes(const uint8_t *kinds, int scale_mode) {
+static size_t factor_bytes(int scale_bits) { return scale_bits == 16 ? 2u : 4u; }
+
+static size_t scale_bytes(const uint8_t *kinds, int scale_mode, int scale_bits) {
   if (!any_int_row(kinds)) return 0;
-  return scale_mode == OR_SCALE_DUAL ? 2u * D128 * 4u : D128 * 4u;
+  return (scale_mode == OR_SCALE_DUAL ? 2u : 1u) * D128 * factor_bytes(scale_bits);
 }
 
-size_t or_block_bytes(const uint8_t *kinds, int unit, int scale_mode) {
-  size_t n = or_code_bytes(kinds, unit) + scale_bytes(kinds, scale_mode);
+size_t or_block_bytes(const uint8_t *kinds, int unit, int scale_mode, int scale_bits) {
+  size_t n = or_code_bytes(kinds, unit) + scale_bytes(kinds, scale_mode, scale_bits);
   return (n + 255u) / 256u * 256u;
 }
 
@@ -353,10 +384,35 @@ static uint32_t field_of(int kind, uint32_t e) {
   return e;   /* FP16 bits or FP32 bits */
 }
 
-void or_encode_block(const uint8_t *kinds, int unit, int scale_mode,
+/* one factor array at block + off: binary32, or the upper halves (bfloat16) */
+static void put_factors(uint8_t *dst, const float *x, int scale_bits) {
+  for (int i = 0; i < D128; ++i) {
+    uint32_t u = f2u(x[i]);
+    if (scale_bits == 16) {
+      uint16_t h = (uint16_t)(u >> 16);
+      memcpy(dst + 2 * i, &h, 2);
+    } else {
+      memcpy(dst + 4 * i, &u, 4);
+    }
+  }
+}
+
+static void get_factors(const uint8_t *src, float *x, int scale_bits) {
+  for (int i = 0; i < D128; ++i) {
+    if (scale_bits == 16) {
+      uint16_t h;
+      memcpy(&h, src + 2 * i, 2);
+      x[i] = u2f((uint32_t)h << 16);
+    } else {
+      memcpy(&x[i], src + 4 * i, 4);
+    }
+  }
+}
+
+void or_encode_block(const uint8_t *kinds, int unit, int scale_mode, int scale_bits,
                      const uint32_t *e, const float *r, const float *c,
                      uint8_t *block) {
-  size_t total = or_block_bytes(kinds, unit, scale_mode);
+  size_t total = or_block_bytes(kinds, unit, scale_mode, scale_bits);
   memset(block, 0, total);
   for (int j = 0; j < D128; ++j) {
     for (int i = 0; i < D128; ++i) {
@@ -370,12 +426,12 @@ void or_encode_block(const uint8_t *kinds, int unit, int scale_mode,
   }
   size_t off = or_code_bytes(kinds, unit);
   if (any_int_row(kinds)) {
-    memcpy(block + off, r, D128 * 4);
-    if (scale_mode == OR_SCALE_DUAL) memcpy(block + off + D128 * 4, c, D128 * 4);
+    put_factors(block + off, r, scale_bits);
+    if (scale_mode == OR_SCALE_DUAL) put_factors(block + off + D128 * factor_bytes(scale_bits), c, scale_bits);
   }
 }
 
-void or_decode_block(const uint8_t *kinds, int unit, int scale_mode,
+void or_decode_block(const uint8_t *kinds, int unit, int scale_mode, int scale_bits,
                      const uint8_t *block, uint32_t *e, float *r, float *c) {
   for (int j = 0; j < D128; ++j) {
     for (int i = 0; i < D128; ++i) {
@@ -394,8 +450,8 @@ void or_decode_block(const uint8_t *kinds, int unit, int scale_mode,
   for (int i = 0; i < D128; ++i) r[i] = 0.0f;
   for (int j = 0; j < D128; ++j) c[j] = 1.0f;
   if (any_int_row(kinds)) {
-    memcpy(r, block + off, D128 * 4);
-    if (scale_mode == OR_SCALE_DUAL) memcpy(c, block + off + D128 * 4, D128 * 4);
+    get_factors(block + off, r, scale_bits);
+    if (scale_mode == OR_SCALE_DUAL) get_factors(block + off + D128 * factor_bytes(scale_bits), c, scale_bits);
   }
 }
 
@@ -404,6 +460,9 @@ void or_decode_block(const uint8_t *kinds, int unit, int scale_mode,
 /* The slot table maps requests to slots ((5B+1) slots per the serving       */
 /* memory accounting quoted in the zhichai.net discussion).                  */
 /* ------------------------------------------------------------------------ */
+/* stored factor width of a pool (0 means binary32) */
+static int SB(const or_pool_desc *desc) { return desc->scale_bits == 16 ? 16 : 32; }
+
 static void head_kinds(const or_pool_desc *desc, int h, uint8_t *out) {
   for (int i = 0; i < D128; ++i)
     out[i] = desc->unit == OR_UNIT_HEAD ? desc->kinds[h]
@@ -417,7 +476,7 @@ int or_pool_layout(const or_pool_desc *desc, uint64_t *head_off,
   for (int h = 0; h < desc->num_heads; ++h) {
     head_kinds(desc, h, kinds);
     if (head_off) head_off[h] = off;
-    off += or_block_bytes(kinds, desc->unit, desc->scale_mode);
+    off += or_block_bytes(kinds, desc->unit, desc->scale_mode, SB(desc));
   }
   if (slot_stride) *slot_stride = off;
   if (total) *total = off * (uint64_t)desc->num_slots;
@@ -464,21 +523,21 @@ static void run_items(work_t *w) {
     size_t boff = (size_t)slot * w->stride + w->head_off[h];
     if (w->op == 0) {
       const float *omega = desc->omega + (size_t)h * D128;
-      or_decode_block(kinds, desc->unit, desc->scale_mode, w->pool + boff, e, r, c);
+      or_decode_block(kinds, desc->unit, desc->scale_mode, SB(desc), w->pool + boff, e, r, c);
       for (int i = 0; i < D128; ++i)
         a[i] = desc->gate == OR_GATE_SCALAR ? w->gate[(size_t)b * H + h] : w->gate[vec + i];
-      or_head_step(D128, kinds, e, r, c, omega, desc->scale_mode, desc->fit_iters,
+      or_head_step(D128, kinds, e, r, c, omega, desc->scale_mode, desc->fit_iters, SB(desc),
                    w->q + vec, w->k + vec, w->v + vec, w->beta[(size_t)b * H + h], a,
                    w->o + vec, NULL);
-      or_encode_block(kinds, desc->unit, desc->scale_mode, e, r, c, w->pool + boff);
+      or_encode_block(kinds, desc->unit, desc->scale_mode, SB(desc), e, r, c, w->pool + boff);
     } else if (w->op == 1) {
       const float *omega = desc->omega + (size_t)h * D128;
       or_requant(D128, kinds, w->S_in + ((size_t)b * H + h) * nn, omega, desc->scale_mode,
-                 desc->fit_iters, e, r, c, NULL);
-      or_encode_block(kinds, desc->unit, desc->scale_mode, e, r, c, w->pool + boff);
+                 desc->fit_iters, SB(desc), e, r, c, NULL);
+      or_encode_block(kinds, desc->unit, desc->scale_mode, SB(desc), e, r, c, w->pool + boff);
     } else {
       for (int i = 0; i < D128; ++i) a[i] = 1.0f;
-      or_decode_block(kinds, desc->unit, desc->scale_mode, w->cpool + boff, e, r, c);
+      or_decode_block(kinds, desc->unit, desc->scale_mode, SB(desc), w->cpool + boff, e, r, c);
       or_dequant(D128, kinds, e, r, c, a, w->S_out + ((size_t)b * H + h) * nn);
     }
   }

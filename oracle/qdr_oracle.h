@@ -67,7 +67,8 @@ void or_delta_update(int d, const float *Sp, const float *k, const float *v,
 void or_readout(int d, const float *S, const float *q, float *o);
 void or_requant(int d, const uint8_t *kinds, const float *S,
                 const float *omega, int scale_mode, int fit_iters,
-                uint32_t *e, float *r, float *c, float *m_out);
+                int scale_bits, uint32_t *e, float *r, float *c,
+                float *m_out);
 float or_fold_sum(float *x, int n);
 
 /* One whole step on a decoded head: dequant+gate, delta update, readout,
@@ -75,18 +76,24 @@ float or_fold_sum(float *x, int n);
  * NULL) receives the updated fp32 state before requantisation. */
 void or_head_step(int d, const uint8_t *kinds, uint32_t *e, float *r,
                   float *c, const float *omega, int scale_mode,
-                  int fit_iters, const float *q, const float *k,
+                  int fit_iters, int scale_bits, const float *q, const float *k,
                   const float *v, float beta, const float *a, float *o,
                   float *S_pre);
 
 /* ---- byte layout of one (slot, head) block, d = 128 --------------------- */
-size_t or_block_bytes(const uint8_t *kinds, int unit, int scale_mode);
+/* scale_bits: 32 stores r and c as binary32, 16 as bfloat16 (the upper 16
+ * bits of the binary32 value, which the factors then are exactly). */
+size_t or_block_bytes(const uint8_t *kinds, int unit, int scale_mode, int scale_bits);
 size_t or_code_bytes(const uint8_t *kinds, int unit);
-void or_encode_block(const uint8_t *kinds, int unit, int scale_mode,
+void or_encode_block(const uint8_t *kinds, int unit, int scale_mode, int scale_bits,
                      const uint32_t *e, const float *r, const float *c,
                      uint8_t *block);
-void or_decode_block(const uint8_t *kinds, int unit, int scale_mode,
+void or_decode_block(const uint8_t *kinds, int unit, int scale_mode, int scale_bits,
                      const uint8_t *block, uint32_t *e, float *r, float *c);
+/* bfloat16 rounding of the factors: up (smallest bfloat16 >= x, x >= 0) and
+ * to nearest (ties to an even last bit). */
+float or_bf16_up(float x);
+float or_bf16_nearest(float x);
 
 /* ---- whole pool (host memory image of the device pool) ------------------ */
 typedef struct {
@@ -94,6 +101,7 @@ typedef struct {
   int32_t unit, gate, scale_mode, fit_iters;
   const uint8_t *kinds;  /* [H] (UNIT_HEAD) or [H*128] (UNIT_ROW) */
   const float *omega;    /* [H*128]                               */
+  int32_t scale_bits;    /* 32 (or 0): binary32 factors; 16: bfloat16 */
 } or_pool_desc;
 
 /* Per-head block offsets inside one slot, the slot stride and total bytes. */

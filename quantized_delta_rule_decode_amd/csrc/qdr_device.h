@@ -198,6 +198,45 @@ __device__ __forceinline__ void store_u32(rsrc_t rs, uint32_t x, uint32_t voff, 
   __builtin_amdgcn_raw_buffer_store_b32((int)x, rs, voff, soff, 0);
 }
 
+// ---- Scale storage.  The SCALE template argument: bit 0 clear = dual-axis
+// factors (r and c), set = per-row absmax (r only); bit 1 set = the factors
+// are stored as bfloat16 instead of fp32.
+constexpr bool dual(int scale) { return (scale & 1) == 0; }
+constexpr bool sc16(int scale) { return (scale & 2) != 0; }
+
+// bfloat16 factors: the row factor and the clip-free column factor round up
+// (toward +inf; x >= 0 finite), so every |Y| <= 1 and every code stays within
+// +-q; a refitted column factor rounds to nearest, ties to even.  The
+// quantiser then uses the rounded value, and the restore reads the same one.
+__device__ __forceinline__ float bf16_up(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t t = u & 0xFFFF0000u;
+  return __uint_as_float((u & 0xFFFFu) ? t + 0x10000u : t);
+}
+
+__device__ __forceinline__ float bf16_nearest(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
+}
+
+// Element i of a factor array that starts at byte `base` of the block.
+template <bool B16>
+__device__ __forceinline__ float load_sc(rsrc_t rs, uint32_t i, uint32_t base) {
+  if constexpr (B16) {
+    const uint32_t h = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, i * 2u, base, 0);
+    return __uint_as_float(h << 16);
+  } else {
+    return load_f32(rs, i * 4u, base);
+  }
+}
+
+// x must be a bfloat16 value when B16 (its low 16 bits are zero).
+template <bool B16>
+__device__ __forceinline__ void store_sc(rsrc_t rs, float x, uint32_t i, uint32_t base) {
+  if constexpr (B16) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(__float_as_uint(x) >> 16), rs, i * 2u, base, 0);
+  else store_f32(rs, x, i * 4u, base);
+}
+
 // Store one column half (this wave's 64 rows of column j) as 16-byte granules.
 // soff0: byte offset of this wave's first granule row; voff = j*16.
 template <int BITS>
@@ -425,7 +464,7 @@ struct Shared : SharedCore {
 // row-absmax baseline).
 template <int BITS, int MODE, int SCALE, int FIT>
 struct Occupancy {
-  static constexpr int waves = (BITS <= 8 && FIT == 0 && SCALE == 0) ? 3 : 2;
+  static constexpr int waves = (BITS <= 8 && FIT == 0 && dual(SCALE)) ? 3 : 2;
 };
 
 // The work of one (request b, head h) of kind BITS; sh is the workgroup's
@@ -439,7 +478,9 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   // INT4 codes convert as z/16 (one SDWA instruction each); the 16 moves into
   // the row factor.  Dual-axis row factors are at most sqrt(FLT_MAX / 2^-40),
   // so 16 g_i stays finite; the row-absmax baseline keeps the plain path.
-  constexpr bool OFF4 = (BITS == 4) && (SCALE == 0);
+  constexpr bool OFF4 = (BITS == 4) && dual(SCALE);
+  constexpr bool SC16 = sc16(SCALE);
+  constexpr uint32_t SCB = SC16 ? 2u : 4u;   // bytes per stored factor
   constexpr float GSCALE = OFF4 ? 16.0f : 1.0f;
 
   const int tid = threadIdx.x;
@@ -462,11 +503,11 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     return;
   }
   uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + head_off;
-  const uint32_t blk_bytes = code_bytes + (INT ? (SCALE == 0 ? 2u : 1u) * kDim * 4u : 0u);
+  const uint32_t blk_bytes = code_bytes + (INT ? (dual(SCALE) ? 2u : 1u) * kDim * SCB : 0u);
   const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(blk, 0, (int)blk_bytes, kRsrcWord3);
   const uint32_t half_off = (uint32_t)w * K::NG * (kDim * 16);   // this wave's first granule row
   const uint32_t r_off = code_bytes;                              // r[128]
-  const uint32_t c_off = code_bytes + kDim * 4;                   // c[128]
+  const uint32_t c_off = code_bytes + kDim * SCB;                 // c[128]
 
   float S[2][64];
   float colc[2] = {1.0f, 1.0f};
@@ -491,11 +532,11 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   }
   if (restores(MODE)) {
     if (INT) {
-      const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
+      const float r_row = load_sc<SC16>(rs, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
       sh.g[row] = (a_row * rn_div(r_row, QMAX)) * GSCALE;
-      if (SCALE == 0) {
-        colc[0] = load_f32(rs, (uint32_t)l * 4u, c_off);
-        colc[1] = load_f32(rs, (uint32_t)l * 4u + 256u, c_off);
+      if (dual(SCALE)) {
+        colc[0] = load_sc<SC16>(rs, (uint32_t)l, c_off);
+        colc[1] = load_sc<SC16>(rs, (uint32_t)l + 64u, c_off);
       }
     } else {
       sh.g[row] = a_row;
@@ -599,7 +640,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   if (INT) {
     // row factor
     float r_row, m_row = 0.0f;
-    if (SCALE == 0) {
+    if (dual(SCALE)) {
       m_row = row_reduce<false>(S, sh.red[w], l) * 0.0078125f;
       const float nu = rn_div(m_row, (P.omega + (size_t)h * kDim)[row]);
       r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
@@ -607,9 +648,10 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       const float mx = row_reduce<true>(S, sh.red[w], l);
       r_row = (mx < FLT_MIN) ? 1.0f : mx;
     }
+    if constexpr (SC16) r_row = bf16_up(r_row);
     sh.ir[row] = rn_div(1.0f, r_row);
     if (FIT) sh.m[row] = m_row;
-    store_f32(rs, r_row, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
+    store_sc<SC16>(rs, r_row, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
     __builtin_amdgcn_wave_barrier();
 
     // Y = S / r (in place) and the column maximum
@@ -633,22 +675,23 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       QDR_FENCE();
     }
     float c0[2] = {1.0f, 1.0f};
-    if (SCALE == 0) {
+    if (dual(SCALE)) {
       sh.cmax[w][l] = fmaxf(cm[0][0], cm[0][1]);
       sh.cmax[w][l + 64] = fmaxf(cm[1][0], cm[1][1]);
     }
     if (is_step(MODE) && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
     __syncthreads();
-    if (SCALE == 0) {
+    if (dual(SCALE)) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const float mx = fmaxf(sh.cmax[0][l + 64 * c], sh.cmax[1][l + 64 * c]);
         c0[c] = (mx < FLT_MIN) ? 1.0f : mx;
+        if constexpr (SC16) c0[c] = bf16_up(c0[c]);
       }
     }
     float wq[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) wq[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) * QMAX : QMAX;
+    for (int c = 0; c < 2; ++c) wq[c] = dual(SCALE) ? rn_div(1.0f, c0[c]) * QMAX : QMAX;
 
     // codes: both columns at once (two independent packing chains), then store
     float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
@@ -696,11 +739,11 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       for (int c = 0; c < 2; ++c) store_column<BITS>(rs, ow[c], (uint32_t)(l + 64 * c) * 16u, half_off);
     }
     // column factor
-    if (SCALE == 0) {
+    if (dual(SCALE)) {
       if (!FIT) {
         if (w == 0) {
-          store_f32(rs, c0[0], (uint32_t)l * 4u, c_off);
-          store_f32(rs, c0[1], (uint32_t)l * 4u + 256u, c_off);
+          store_sc<SC16>(rs, c0[0], (uint32_t)l, c_off);
+          store_sc<SC16>(rs, c0[1], (uint32_t)l + 64u, c_off);
         }
       } else {
         if (w == 0) {
@@ -725,7 +768,9 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
                 dd = __builtin_fmaf(pz, zeta, dd);
               }
             }
-            store_f32(rs, (dd > 0.0f) ? rn_div(nn, dd) : c0[c], (uint32_t)l * 4u + 256u * c, c_off);
+            float cf = (dd > 0.0f) ? rn_div(nn, dd) : c0[c];
+            if constexpr (SC16) cf = bf16_nearest(cf);
+            store_sc<SC16>(rs, cf, (uint32_t)l + 64u * c, c_off);
           }
         }
       }
@@ -904,12 +949,14 @@ k_rows(const LaunchArgs P) {
     return;
   }
   uint8_t *blk = P.pool + (size_t)slot * P.slot_stride + blk_off;
-  const uint32_t blk_bytes = code_bytes + (has_int ? (SCALE == 0 ? 2u : 1u) * kDim * 4u : 0u);
+  constexpr bool SC16 = sc16(SCALE);
+  constexpr uint32_t SCB = SC16 ? 2u : 4u;   // bytes per stored factor
+  const uint32_t blk_bytes = code_bytes + (has_int ? (dual(SCALE) ? 2u : 1u) * kDim * SCB : 0u);
   const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(blk, 0, (int)blk_bytes, kRsrcWord3);
   const int nwords = (w == 0) ? words0 : words1;                    // words per column, this half
   const uint32_t half_off = (w == 0) ? 0u : (uint32_t)words0 * (kDim * 4);
   const uint32_t half_bytes = (uint32_t)nwords * (kDim * 4);
-  const uint32_t r_off = code_bytes, c_off = code_bytes + kDim * 4;
+  const uint32_t r_off = code_bytes, c_off = code_bytes + kDim * SCB;
   uint32_t *codes = lds_codes + (size_t)w * P.region_rows * kDim;   // [word][column]
   uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
   const uint32_t lane_byte = (uint32_t)l * 4u;                       // column l of word 0
@@ -943,14 +990,14 @@ k_rows(const LaunchArgs P) {
   if (has_readout(MODE)) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
   if (restores(MODE)) {
     if (my_int) {
-      const float r_row = load_f32(rs, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
+      const float r_row = load_sc<SC16>(rs, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
       sh.g[row] = a_row * rn_div(r_row, my_q);
     } else {
       sh.g[row] = a_row;
     }
-    if (SCALE == 0 && has_int) {
-      colc[0] = load_f32(rs, (uint32_t)l * 4u, c_off);
-      colc[1] = load_f32(rs, (uint32_t)l * 4u + 256u, c_off);
+    if (dual(SCALE) && has_int) {
+      colc[0] = load_sc<SC16>(rs, (uint32_t)l, c_off);
+      colc[1] = load_sc<SC16>(rs, (uint32_t)l + 64u, c_off);
     }
   }
   float vcol[2] = {0.0f, 0.0f};
@@ -1078,7 +1125,7 @@ k_rows(const LaunchArgs P) {
   // passed the barrier after their restore, so no staged word is read again)
   float (*red)[20] = reinterpret_cast<float (*)[20]>(codes);
   float r_row = 0.0f, m_row = 0.0f;
-  if (SCALE == 0) {
+  if (dual(SCALE)) {
     m_row = row_reduce<false>(S, red, l) * 0.0078125f;
     const float nu = rn_div(m_row, (P.omega + (size_t)h * kDim)[row]);
     r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
@@ -1086,6 +1133,7 @@ k_rows(const LaunchArgs P) {
     const float mx = row_reduce<true>(S, red, l);
     r_row = (mx < FLT_MIN) ? 1.0f : mx;
   }
+  if constexpr (SC16) r_row = bf16_up(r_row);
   if (!my_int) { r_row = 0.0f; m_row = 0.0f; }
   // pivot rows keep their values through the Y pass (factor 1) and are
   // excluded from the column maximum (flag 0)
@@ -1115,22 +1163,23 @@ k_rows(const LaunchArgs P) {
     }
       }
   float c0[2] = {1.0f, 1.0f};
-  if (SCALE == 0) {
+  if (dual(SCALE)) {
     sh.cmax[w][l] = cm[0];
     sh.cmax[w][l + 64] = cm[1];
   }
   if (is_step(MODE) && w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
   __syncthreads();
-  if (SCALE == 0) {
+  if (dual(SCALE)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const float mx = fmaxf(sh.cmax[0][l + 64 * c], sh.cmax[1][l + 64 * c]);
       c0[c] = (mx < FLT_MIN) ? 1.0f : mx;
+      if constexpr (SC16) c0[c] = bf16_up(c0[c]);
     }
   }
   float ec[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) ec[c] = (SCALE == 0) ? rn_div(1.0f, c0[c]) : 1.0f;
+  for (int c = 0; c < 2; ++c) ec[c] = dual(SCALE) ? rn_div(1.0f, c0[c]) : 1.0f;
 
   // ---------------- codes.  Pivot rows first leave their stored bits (fp16
   // or fp32 of S) in LDS; P1 turns every value into its code bits in place
@@ -1153,7 +1202,7 @@ k_rows(const LaunchArgs P) {
   // V1a refit sums: fma chains over the integer rows in ascending order, so
   // wave 1 starts from wave 0's totals over rows 0..63 (it waits for them)
   float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
-  if (FIT && SCALE == 0 && w == 1) {
+  if (FIT && dual(SCALE) && w == 1) {
     __syncthreads();
     nacc[0] = sh.d[l]; nacc[1] = sh.d[l + 64];
     dacc[0] = sh.y[l]; dacc[1] = sh.y[l + 64];
@@ -1185,7 +1234,7 @@ k_rows(const LaunchArgs P) {
       }
     }
       }
-  if (FIT && SCALE == 0 && w == 0) {
+  if (FIT && dual(SCALE) && w == 0) {
     sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
     sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];
     __syncthreads();
@@ -1250,18 +1299,21 @@ k_rows(const LaunchArgs P) {
 
   // ---------------- row and column factors (stored after every read of the
   // row tables, so those stay scalar loads)
-  if (has_int) store_f32(rs, r_row, (uint32_t)l * 4u, r_off + (uint32_t)w * 256u);
-  if (SCALE == 0 && has_int) {
+  if (has_int) store_sc<SC16>(rs, r_row, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
+  if (dual(SCALE) && has_int) {
     if (!FIT) {
       if (w == 0) {
-        store_f32(rs, c0[0], (uint32_t)l * 4u, c_off);
-        store_f32(rs, c0[1], (uint32_t)l * 4u + 256u, c_off);
+        store_sc<SC16>(rs, c0[0], (uint32_t)l, c_off);
+        store_sc<SC16>(rs, c0[1], (uint32_t)l + 64u, c_off);
       }
     } else if (w == 1) {
       // wave 1 holds the sums over all integer rows
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        store_f32(rs, (dacc[c] > 0.0f) ? rn_div(nacc[c], dacc[c]) : c0[c], (uint32_t)l * 4u + 256u * c, c_off);
+      for (int c = 0; c < 2; ++c) {
+        float cf = (dacc[c] > 0.0f) ? rn_div(nacc[c], dacc[c]) : c0[c];
+        if constexpr (SC16) cf = bf16_nearest(cf);
+        store_sc<SC16>(rs, cf, (uint32_t)l + 64u * c, c_off);
+      }
     }
   }
 
@@ -1278,26 +1330,46 @@ k_rows(const LaunchArgs P) {
 // --------------------------------------------------------------------------
 namespace {
 
+// Calls f(GATE, SCALE, FIT) -- each a std::integral_constant -- with the
+// template arguments of the pool: the gate form, the scale mode and width
+// (SCALE bit 0: row absmax, bit 1: bfloat16 factors) and the refit (dual-axis
+// scales only).
+template <class F>
+void with_variant(const PoolConfig &cfg, F &&f) {
+  using std::integral_constant;
+  const bool diag = cfg.gate == 1, fit = cfg.fit_iters > 0;
+  const int s = (cfg.scale_mode == 0 ? 0 : 1) | (cfg.scale_bits == 16 ? 2 : 0);
+  auto go = [&](auto g) {
+    switch (s) {
+      case 0:
+        if (fit) f(g, integral_constant<int, 0>{}, integral_constant<int, 1>{});
+        else f(g, integral_constant<int, 0>{}, integral_constant<int, 0>{});
+        break;
+      case 1: f(g, integral_constant<int, 1>{}, integral_constant<int, 0>{}); break;
+      case 2:
+        if (fit) f(g, integral_constant<int, 2>{}, integral_constant<int, 1>{});
+        else f(g, integral_constant<int, 2>{}, integral_constant<int, 0>{});
+        break;
+      default: f(g, integral_constant<int, 3>{}, integral_constant<int, 0>{}); break;
+    }
+  };
+  if (diag) go(integral_constant<int, 1>{});
+  else go(integral_constant<int, 0>{});
+}
+
 template <int BITS, int MODE>
 hipError_t launch_head_kind(const PoolConfig &cfg, const LaunchArgs &a, int n, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)n * a.n_list)), block(128);
   if (grid.x == 0) return hipSuccess;
-  const bool dual = cfg.scale_mode == 0;
-  const bool fit = cfg.fit_iters > 0;
-  const bool diag = cfg.gate == 1;
-  if (!Kind<BITS>::is_int) {
-    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 0>), grid, block, 0, st, a);
+  if (!Kind<BITS>::is_int) {   // float kinds store no factors
+    if (cfg.gate == 1) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 0>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 0, 0>), grid, block, 0, st, a);
-  } else if (!dual) {
-    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 1, 0>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 1, 0>), grid, block, 0, st, a);
-  } else if (fit) {
-    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 1>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 0, 1>), grid, block, 0, st, a);
-  } else {
-    if (diag) hipLaunchKernelGGL((k_head<BITS, MODE, 1, 0, 0>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_head<BITS, MODE, 0, 0, 0>), grid, block, 0, st, a);
+    return hipGetLastError();
   }
+  with_variant(cfg, [&](auto G, auto S, auto Fi) {
+    hipLaunchKernelGGL((k_head<BITS, MODE, decltype(G)::value, decltype(S)::value, decltype(Fi)::value>), grid,
+                       block, 0, st, a);
+  });
   return hipGetLastError();
 }
 
@@ -1305,19 +1377,10 @@ template <int MODE>
 hipError_t launch_head_int_mode(const PoolConfig &cfg, const LaunchArgs &a, int n, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)n * a.n_list)), block(128);
   if (grid.x == 0) return hipSuccess;
-  const bool dual = cfg.scale_mode == 0;
-  const bool fit = cfg.fit_iters > 0;
-  const bool diag = cfg.gate == 1;
-  if (!dual) {
-    if (diag) hipLaunchKernelGGL((k_head_int<MODE, 1, 1, 0>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_head_int<MODE, 0, 1, 0>), grid, block, 0, st, a);
-  } else if (fit) {
-    if (diag) hipLaunchKernelGGL((k_head_int<MODE, 1, 0, 1>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_head_int<MODE, 0, 0, 1>), grid, block, 0, st, a);
-  } else {
-    if (diag) hipLaunchKernelGGL((k_head_int<MODE, 1, 0, 0>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_head_int<MODE, 0, 0, 0>), grid, block, 0, st, a);
-  }
+  with_variant(cfg, [&](auto G, auto S, auto Fi) {
+    hipLaunchKernelGGL((k_head_int<MODE, decltype(G)::value, decltype(S)::value, decltype(Fi)::value>), grid,
+                       block, 0, st, a);
+  });
   return hipGetLastError();
 }
 

@@ -71,6 +71,7 @@ struct LaunchArgs {
 
 struct PoolConfig {
   int unit, gate, scale_mode, fit_iters;
+  int scale_bits;             // 32: fp32 factors; 16: bfloat16
   int max_words;              // row units: largest words-per-column of any half
   int max_pivots;             // row units: most FP16/FP32 rows in any half
 };

@@ -20,26 +20,17 @@ hipError_t launch_rows(const PoolConfig &cfg, LaunchArgs a, int n, const ListEnt
   const size_t lds = (size_t)2 * a.region_rows * kDim * sizeof(uint32_t);
   const dim3 grid((unsigned)((int64_t)n * count)), block(128);
   if (grid.x == 0) return hipSuccess;
-  const bool dual = cfg.scale_mode == 0, fit = cfg.fit_iters > 0, diag = cfg.gate == 1;
-  if (lds > 65536) {   // pools with FP32 rows: allow the larger dynamic LDS
-    const void *fns[6] = {(const void *)k_rows<MODE, 1, 1, 0>, (const void *)k_rows<MODE, 0, 1, 0>,
-                          (const void *)k_rows<MODE, 1, 0, 1>, (const void *)k_rows<MODE, 0, 0, 1>,
-                          (const void *)k_rows<MODE, 1, 0, 0>, (const void *)k_rows<MODE, 0, 0, 0>};
-    for (const void *f : fns) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
+  hipError_t err = hipSuccess;
+  with_variant(cfg, [&](auto G, auto S, auto Fi) {
+    const void *fn = (const void *)k_rows<MODE, decltype(G)::value, decltype(S)::value, decltype(Fi)::value>;
+    if (lds > 65536) {   // pools with FP32 rows: allow the larger dynamic LDS
+      err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return;
     }
-  }
-  if (!dual) {
-    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 1, 0>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((k_rows<MODE, 0, 1, 0>), grid, block, lds, st, a);
-  } else if (fit) {
-    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 1>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 1>), grid, block, lds, st, a);
-  } else {
-    if (diag) hipLaunchKernelGGL((k_rows<MODE, 1, 0, 0>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((k_rows<MODE, 0, 0, 0>), grid, block, lds, st, a);
-  }
+    hipLaunchKernelGGL((k_rows<MODE, decltype(G)::value, decltype(S)::value, decltype(Fi)::value>), grid, block,
+                       lds, st, a);
+  });
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 

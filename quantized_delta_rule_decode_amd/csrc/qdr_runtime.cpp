@@ -84,6 +84,8 @@ qdr_status check_desc(const qdr_pool_desc *d) {
   if (d->fit_iters < 0 || d->fit_iters > 1) return fail(QDR_E_INVAL, "fit_iters must be 0 or 1");
   if (d->fit_iters > 0 && d->scale_mode != QDR_SCALE_DUAL)
     return fail(QDR_E_INVAL, "fit_iters requires dual-axis scales");
+  if (d->scale_bits != 0 && d->scale_bits != 32 && d->scale_bits != 16)
+    return fail(QDR_E_INVAL, "scale_bits must be 0, 32 or 16 (got %d)", d->scale_bits);
   if (!d->kinds) return fail(QDR_E_INVAL, "kinds is NULL");
   const int64_t nk = d->unit == QDR_UNIT_HEAD ? d->num_heads : (int64_t)d->num_heads * QDR_DIM;
   for (int64_t i = 0; i < nk; ++i)
@@ -147,7 +149,8 @@ void build_layout(const qdr_pool_desc *d, HostLayout &L) {
       if (words > L.max_words) L.max_words = words;
     }
     const uint64_t code = ng * QDR_DIM * G;
-    const uint64_t scales = any_int ? (d->scale_mode == QDR_SCALE_DUAL ? 2 * QDR_DIM * 4 : QDR_DIM * 4) : 0;
+    const uint64_t fb = d->scale_bits == 16 ? 2 : 4;   // bytes per stored factor
+    const uint64_t scales = any_int ? (d->scale_mode == QDR_SCALE_DUAL ? 2 * QDR_DIM * fb : QDR_DIM * fb) : 0;
     const uint64_t blk = (code + scales + 255) / 256 * 256;
     L.head_off[h] = off;
     L.head_bytes[h] = (uint32_t)blk;
@@ -306,6 +309,7 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
   p->cfg.gate = desc->gate;
   p->cfg.scale_mode = desc->scale_mode;
   p->cfg.fit_iters = desc->fit_iters;
+  p->cfg.scale_bits = desc->scale_bits == 16 ? 16 : 32;
   p->cfg.max_words = p->L.max_words;
   p->cfg.max_pivots = p->L.max_pivots;
   if (hipGetDevice(&p->device) != hipSuccess) { free_pool(p); return fail(QDR_E_DEVICE, "no HIP device"); }

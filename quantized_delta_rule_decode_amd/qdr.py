@@ -37,7 +37,8 @@ class PoolDesc(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("unit", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("scale_mode", ctypes.c_int32), ("fit_iters", ctypes.c_int32),
-                ("kinds", ctypes.c_void_p), ("omega", ctypes.c_void_p)]
+                ("kinds", ctypes.c_void_p), ("omega", ctypes.c_void_p),
+                ("scale_bits", ctypes.c_int32)]
 
 
 class Layout(ctypes.Structure):
@@ -118,17 +119,17 @@ def _dptr(t, dtype, name, numel=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _desc(num_slots, num_heads, kinds, omega, unit, gate, scale_mode, fit_iters):
+def _desc(num_slots, num_heads, kinds, omega, unit, gate, scale_mode, fit_iters, scale_bits=32):
     kinds = np.ascontiguousarray(kinds, np.uint8)
     om = None if omega is None else np.ascontiguousarray(omega, np.float32)
     d = PoolDesc(num_slots, num_heads, DIM, DIM, unit, gate, scale_mode, fit_iters,
-                 kinds.ctypes.data, None if om is None else om.ctypes.data)
+                 kinds.ctypes.data, None if om is None else om.ctypes.data, scale_bits)
     return d, (kinds, om)
 
 
 def qdr_pool_bytes(num_slots, num_heads, kinds, omega, unit=UNIT_HEAD, gate=GATE_SCALAR,
-                   scale_mode=SCALE_DUAL, fit_iters=0) -> int:
-    d, keep = _desc(num_slots, num_heads, kinds, omega, unit, gate, scale_mode, fit_iters)
+                   scale_mode=SCALE_DUAL, fit_iters=0, scale_bits=32) -> int:
+    d, keep = _desc(num_slots, num_heads, kinds, omega, unit, gate, scale_mode, fit_iters, scale_bits)
     n = ctypes.c_size_t(0)
     _check("qdr_pool_bytes", load().qdr_pool_bytes(ctypes.byref(d), ctypes.byref(n)))
     return int(n.value)
@@ -138,10 +139,11 @@ class Pool:
     """A state pool (qdr_pool_create ... qdr_pool_destroy)."""
 
     def __init__(self, num_slots, num_heads, kinds, omega, unit=UNIT_HEAD, gate=GATE_SCALAR,
-                 scale_mode=SCALE_DUAL, fit_iters=0, dev_mem=None):
+                 scale_mode=SCALE_DUAL, fit_iters=0, dev_mem=None, scale_bits=32):
         self.num_slots, self.num_heads = int(num_slots), int(num_heads)
         self.unit, self.gate, self.scale_mode, self.fit_iters = unit, gate, scale_mode, fit_iters
-        d, keep = _desc(num_slots, num_heads, kinds, omega, unit, gate, scale_mode, fit_iters)
+        self.scale_bits = scale_bits
+        d, keep = _desc(num_slots, num_heads, kinds, omega, unit, gate, scale_mode, fit_iters, scale_bits)
         h = ctypes.c_void_p(None)
         mem_ptr, mem_bytes = None, 0
         if dev_mem is not None:

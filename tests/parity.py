@@ -56,9 +56,9 @@ def _tie_analysis(orc, orc_pool, h, S, blk_ref, blk_dev):
     Returns (n_codes_differing, n_excusable, other_bytes_differ).
     """
     kinds = orc_pool.head_kinds(h)
-    unit, mode = orc_pool.unit, orc_pool.scale_mode
-    e_ref, r_ref, c_ref = orc.decode_block(kinds, unit, mode, blk_ref)
-    e_dev, r_dev, c_dev = orc.decode_block(kinds, unit, mode, blk_dev)
+    unit, mode, sb = orc_pool.unit, orc_pool.scale_mode, orc_pool.scale_bits
+    e_ref, r_ref, c_ref = orc.decode_block(kinds, unit, mode, blk_ref, scale_bits=sb)
+    e_dev, r_dev, c_dev = orc.decode_block(kinds, unit, mode, blk_dev, scale_bits=sb)
     introw = np.array([kk <= 8 for kk in kinds])
     diff = e_ref != e_dev
     other = bool(np.any(diff[~introw])) or not np.array_equal(r_ref, r_dev) \
@@ -73,6 +73,8 @@ def _tie_analysis(orc, orc_pool, h, S, blk_ref, blk_dev):
     if mode == 0:
         mx = np.max(np.abs(np.where(introw[:, None], Y, np.float32(0))), axis=0).astype(np.float32)
         c0 = np.where(mx < np.finfo(np.float32).tiny, np.float32(1), mx).astype(np.float32)
+        if sb == 16:   # the clip-free column factor is stored rounded up to bfloat16
+            c0 = np.array([orc.bf16_up(float(x)) for x in c0], np.float32)
     else:
         c0 = np.ones(D, np.float32)
     e = (np.float32(1.0) / c0).astype(np.float32)
@@ -137,11 +139,13 @@ def step_state_fn(orc, orc_pool, prev_mem, slots, inputs):
         off = slot * orc_pool.slot_stride + int(orc_pool.head_off[h])
         blk = prev_mem[off: off + orc_pool.block_size(h)]
         kinds = orc_pool.head_kinds(h)
-        e0, r0, c0 = orc.decode_block(kinds, orc_pool.unit, orc_pool.scale_mode, blk)
+        e0, r0, c0 = orc.decode_block(kinds, orc_pool.unit, orc_pool.scale_mode, blk,
+                                      scale_bits=orc_pool.scale_bits)
         a = np.full(D, gate[b, h], np.float32) if gate.ndim == 2 else gate[b, h]
         _, _, _, _, S = orc.head_step(kinds, e0, r0, c0, orc_pool.omega[h], q[b, h], k[b, h],
                                       v[b, h], float(beta[b, h]), a,
-                                      scale_mode=orc_pool.scale_mode, fit_iters=orc_pool.fit_iters)
+                                      scale_mode=orc_pool.scale_mode, fit_iters=orc_pool.fit_iters,
+                                      scale_bits=orc_pool.scale_bits)
         return S
     return state_of
 

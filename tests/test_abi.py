@@ -40,14 +40,15 @@ def _bytes(**kw):
     return qdr.qdr_pool_bytes(**kw)
 
 
+@pytest.mark.parametrize("sb", [32, 16])
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_pool_bytes_match_oracle_layout(orc, lib, cid):
+def test_pool_bytes_match_oracle_layout(orc, lib, cid, sb):
     cfg = synth.CONFIGS[cid]
     t = synth.static_tables(cfg)
     n = _bytes(num_slots=cfg.num_slots, num_heads=cfg.H, kinds=t["kinds"], omega=t["omega"],
-               unit=cfg.unit, gate=cfg.gate, scale_mode=cfg.scale_mode)
+               unit=cfg.unit, gate=cfg.gate, scale_mode=cfg.scale_mode, scale_bits=sb)
     P = orc.Pool(cfg.num_slots, cfg.H, t["kinds"], t["omega"], unit=cfg.unit, gate=cfg.gate,
-                 scale_mode=cfg.scale_mode)
+                 scale_mode=cfg.scale_mode, scale_bits=sb)
     assert n == P.total
 
 
@@ -63,7 +64,8 @@ def test_config4_pool_size():
 
 @pytest.mark.parametrize("bad", [
     dict(num_slots=0), dict(num_heads=0), dict(unit=2), dict(gate=5), dict(scale_mode=3),
-    dict(fit_iters=2), dict(fit_iters=1, scale_mode=1), dict(kinds_value=5), dict(omega_value=0.0),
+    dict(fit_iters=2), dict(fit_iters=1, scale_mode=1), dict(scale_bits=8), dict(scale_bits=-16),
+    dict(kinds_value=5), dict(omega_value=0.0),
     dict(omega_value=float("nan")), dict(omega_value=2.0 ** 41), dict(omega_none=True),
 ])
 def test_descriptor_errors(lib, bad):
@@ -86,6 +88,7 @@ def test_descriptor_errors(lib, bad):
 
 def test_row_absmax_needs_no_omega(lib):
     assert _bytes(num_slots=1, num_heads=1, kinds=[8], omega=None, scale_mode=1) == 16384 + 512
+    assert _bytes(num_slots=1, num_heads=1, kinds=[8], omega=None, scale_mode=1, scale_bits=16) == 16384 + 256
 
 
 def test_null_arguments_rejected(lib):

@@ -54,24 +54,29 @@ HEAD_KIND_SETS = {
 }
 
 
-def make_pair(orc, num_slots, kinds, omega, unit=0, gate=0, scale=0, fit=0):
+def make_pair(orc, num_slots, kinds, omega, unit=0, gate=0, scale=0, fit=0, sb=32):
     H = len(kinds) if unit == 0 else len(kinds) // D
-    dev = qdr.Pool(num_slots, H, kinds, omega, unit=unit, gate=gate, scale_mode=scale, fit_iters=fit)
+    dev = qdr.Pool(num_slots, H, kinds, omega, unit=unit, gate=gate, scale_mode=scale, fit_iters=fit,
+                   scale_bits=sb)
     ref = orc.Pool(num_slots, H, kinds, omega, unit=unit, gate=gate, scale_mode=scale,
-                   fit_iters=fit).alloc()
+                   fit_iters=fit, scale_bits=sb).alloc()
     assert dev.slot_stride == ref.slot_stride
     assert np.array_equal(dev.head_off, ref.head_off.astype(np.uint64))
     return dev, ref
 
 
+SB = pytest.mark.parametrize("sb", [32, 16])
+
+
+@SB
 @pytest.mark.parametrize("name", sorted(HEAD_KIND_SETS))
 @pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
-def test_pack_parity(torch_dev, orc, name, scale, fit):
+def test_pack_parity(torch_dev, orc, name, scale, fit, sb):
     torch = torch_dev
     kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
     H = kinds.size
     omega = np.random.default_rng(1).lognormal(0, 1, (H, D)).astype(np.float32)
-    dev, ref = make_pair(orc, 5, kinds, omega, scale=scale, fit=fit)
+    dev, ref = make_pair(orc, 5, kinds, omega, scale=scale, fit=fit, sb=sb)
     slots = np.array([3, 0, 4], np.int32)
     S = edge_states(7, 3, H)
     dev.qdr_pack(t_(torch, slots), t_(torch, S))
@@ -79,18 +84,19 @@ def test_pack_parity(torch_dev, orc, name, scale, fit):
     torch.cuda.synchronize()
     rep = parity.StepReport()
     parity.compare_pool(orc, ref, dev, slots, lambda b, h: S[b, h], rep, resync=False)
-    parity.assert_step_ok(rep, f"pack {name} scale={scale} fit={fit}")
+    parity.assert_step_ok(rep, f"pack {name} scale={scale} fit={fit} sb={sb}")
     assert rep.blocks_mismatched == 0
 
 
+@SB
 @pytest.mark.parametrize("name", sorted(HEAD_KIND_SETS))
 @pytest.mark.parametrize("scale", [0, 1])
-def test_unpack_parity(torch_dev, orc, name, scale):
+def test_unpack_parity(torch_dev, orc, name, scale, sb):
     torch = torch_dev
     kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
     H = kinds.size
     omega = np.random.default_rng(2).lognormal(0, 1, (H, D)).astype(np.float32)
-    dev, ref = make_pair(orc, 3, kinds, omega, scale=scale)
+    dev, ref = make_pair(orc, 3, kinds, omega, scale=scale, sb=sb)
     S = edge_states(8, 3, H)
     ref.pack(np.arange(3, dtype=np.int32), S)
     for s in range(3):
@@ -103,12 +109,13 @@ def test_unpack_parity(torch_dev, orc, name, scale):
     assert np.array_equal(X_dev.view(np.uint32), X_ref.view(np.uint32))
 
 
-def test_reset_encodes_zero(torch_dev, orc):
+@SB
+def test_reset_encodes_zero(torch_dev, orc, sb):
     torch = torch_dev
     kinds = np.array([2, 4, 6, 8, 16, 32], np.uint8)
     omega = np.ones((6, D), np.float32)
     for scale in (0, 1):
-        dev, ref = make_pair(orc, 4, kinds, omega, scale=scale)
+        dev, ref = make_pair(orc, 4, kinds, omega, scale=scale, sb=sb)
         slots = np.array([1, 3], np.int32)
         dev.qdr_slot_reset(t_(torch, slots))
         ref.pack(slots, np.zeros((2, 6, D, D), np.float32))
@@ -141,15 +148,16 @@ def run_step_pair(torch, orc, dev, ref, slots, inputs, threads=8):
     return rep, o_dev, o_ref, bad
 
 
+@SB
 @pytest.mark.parametrize("name", sorted(HEAD_KIND_SETS))
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
-def test_single_step_parity(torch_dev, orc, name, gate, scale, fit):
+def test_single_step_parity(torch_dev, orc, name, gate, scale, fit, sb):
     torch = torch_dev
     kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
     H = kinds.size
     omega = np.random.default_rng(3).lognormal(0, 1, (H, D)).astype(np.float32)
-    dev, ref = make_pair(orc, 6, kinds, omega, gate=gate, scale=scale, fit=fit)
+    dev, ref = make_pair(orc, 6, kinds, omega, gate=gate, scale=scale, fit=fit, sb=sb)
     S = edge_states(11, 6, H)
     all_slots = np.arange(6, dtype=np.int32)
     dev.qdr_pack(t_(torch, all_slots), t_(torch, S))
@@ -157,7 +165,7 @@ def test_single_step_parity(torch_dev, orc, name, gate, scale, fit):
     slots = np.array([4, -1, 0, 5, 2], np.int32)     # padding row and a ragged subset
     inputs = random_inputs(12, slots.size, H, gate == 1)
     rep, o_dev, o_ref, bad = run_step_pair(torch, orc, dev, ref, slots, inputs)
-    parity.assert_step_ok(rep, f"step {name} gate={gate} scale={scale} fit={fit}")
+    parity.assert_step_ok(rep, f"step {name} gate={gate} scale={scale} fit={fit} sb={sb}")
     assert bad == 0
     assert np.all(o_dev[1] == 0)
     # untouched slots keep their bytes
@@ -208,13 +216,13 @@ def test_deterministic(torch_dev, orc):
 
 
 # ----------------------------------------------------------------- configs
-def trajectory(torch, orc, cid, steps, threads=16):
+def trajectory(torch, orc, cid, steps, threads=16, sb=32):
     from quantized_delta_rule_decode_amd import workload
     cfg = synth.CONFIGS[cid]
     t = synth.static_tables(cfg)
-    dev = workload.make_pool(cfg, t)
+    dev = workload.make_pool(cfg, t, scale_bits=sb)
     ref = orc.Pool(cfg.num_slots, cfg.H, t["kinds"], t["omega"], unit=cfg.unit, gate=cfg.gate,
-                   scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters).alloc()
+                   scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters, scale_bits=sb).alloc()
     slots = t["slots"]
     slots_t = t_(torch, slots)
     if cfg.warmup:
@@ -262,6 +270,11 @@ def test_config2_trajectory(torch_dev, orc):
     assert worst <= 1e-4
 
 
+def test_config2_trajectory_bf16_scales(torch_dev, orc):
+    worst, excused = trajectory(torch_dev, orc, 2, 24, sb=16)
+    assert worst <= 1e-4
+
+
 # ----------------------------------------------------------------- row units (KDA)
 def row_kinds(name, H, seed=0):
     g = np.random.default_rng(seed)
@@ -281,14 +294,15 @@ def row_kinds(name, H, seed=0):
 ROW_SETS = ["kda_mix", "fp32_rows", "float_only_head", "straddle"]
 
 
+@SB
 @pytest.mark.parametrize("name", ROW_SETS)
 @pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
-def test_rows_pack_unpack_parity(torch_dev, orc, name, scale, fit):
+def test_rows_pack_unpack_parity(torch_dev, orc, name, scale, fit, sb):
     torch = torch_dev
     H = 3
     kinds = row_kinds(name, H, 5)
     omega = np.random.default_rng(6).lognormal(0, 1, (H, D)).astype(np.float32)
-    dev, ref = make_pair(orc, 4, kinds, omega, unit=1, gate=1, scale=scale, fit=fit)
+    dev, ref = make_pair(orc, 4, kinds, omega, unit=1, gate=1, scale=scale, fit=fit, sb=sb)
     slots = np.array([2, 0, 3], np.int32)
     S = edge_states(13, 3, H, kinds.reshape(H, D) == 16)
     dev.qdr_pack(t_(torch, slots), t_(torch, S))
@@ -296,7 +310,7 @@ def test_rows_pack_unpack_parity(torch_dev, orc, name, scale, fit):
     torch.cuda.synchronize()
     rep = parity.StepReport()
     parity.compare_pool(orc, ref, dev, slots, lambda b, h: S[b, h], rep, resync=False)
-    parity.assert_step_ok(rep, f"rows pack {name} scale={scale} fit={fit}")
+    parity.assert_step_ok(rep, f"rows pack {name} scale={scale} fit={fit} sb={sb}")
     assert rep.blocks_mismatched == 0
     # restore from the (identical) packed bytes
     out = torch.full((3, H, D, D), 5.0, dtype=torch.float32, device="cuda")
@@ -310,15 +324,16 @@ def test_rows_pack_unpack_parity(torch_dev, orc, name, scale, fit):
     assert np.array_equal(dev.qdr_read_raw(1), ref.mem[ref.slot_stride:2 * ref.slot_stride])
 
 
+@SB
 @pytest.mark.parametrize("name", ROW_SETS)
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("scale,fit", [(0, 0), (1, 0), (0, 1)])
-def test_rows_step_parity(torch_dev, orc, name, gate, scale, fit):
+def test_rows_step_parity(torch_dev, orc, name, gate, scale, fit, sb):
     torch = torch_dev
     H = 3
     kinds = row_kinds(name, H, 7)
     omega = np.random.default_rng(8).lognormal(0, 1, (H, D)).astype(np.float32)
-    dev, ref = make_pair(orc, 5, kinds, omega, unit=1, gate=gate, scale=scale, fit=fit)
+    dev, ref = make_pair(orc, 5, kinds, omega, unit=1, gate=gate, scale=scale, fit=fit, sb=sb)
     S = edge_states(17, 5, H, kinds.reshape(H, D) == 16)
     all_slots = np.arange(5, dtype=np.int32)
     dev.qdr_pack(t_(torch, all_slots), t_(torch, S))
@@ -326,7 +341,7 @@ def test_rows_step_parity(torch_dev, orc, name, gate, scale, fit):
     slots = np.array([3, -1, 1, 4], np.int32)
     inputs = random_inputs(18, slots.size, H, gate == 1)
     rep, o_dev, o_ref, bad = run_step_pair(torch, orc, dev, ref, slots, inputs)
-    parity.assert_step_ok(rep, f"rows step {name} gate={gate} scale={scale} fit={fit}")
+    parity.assert_step_ok(rep, f"rows step {name} gate={gate} scale={scale} fit={fit} sb={sb}")
     assert bad == 0 and np.all(o_dev[1] == 0)
     for s in (0, 2):
         assert np.array_equal(dev.qdr_read_raw(s), ref.mem[s * ref.slot_stride:(s + 1) * ref.slot_stride])
@@ -334,4 +349,9 @@ def test_rows_step_parity(torch_dev, orc, name, gate, scale, fit):
 
 def test_config3_trajectory(torch_dev, orc):
     worst, excused = trajectory(torch_dev, orc, 3, 12)
+    assert worst <= 1e-4
+
+
+def test_config3_trajectory_bf16_scales(torch_dev, orc):
+    worst, excused = trajectory(torch_dev, orc, 3, 6, sb=16)
     assert worst <= 1e-4

@@ -176,6 +176,10 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) dword access on CDNA
 
 // Code granules are read once per step: nontemporal (nt) loads.
+// A lane offset past every block's buffer range: a raw buffer load there
+// returns zeros without touching memory.
+constexpr uint32_t kBeyondBuffer = 0x80000000u;
+
 __device__ __forceinline__ uint4 load_granule(rsrc_t rs, uint32_t voff, uint32_t soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 2);
   return make_uint4(v[0], v[1], v[2], v[3]);
@@ -850,13 +854,13 @@ k_head_int(const LaunchArgs P) {
   else head_body<2, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
 }
 
-typedef const __attribute__((address_space(4))) RowProg *const_rowprog_t;
-
-// entry i of a row table, copied field by field out of the constant space
-__device__ __forceinline__ RowProg row_op(const_rowprog_t p, int i) {
+// Row i's program entry, broadcast from lane i of the per-lane table
+// registers (i is a compile-time lane index, so each field is one v_readlane
+// into a scalar register).
+__device__ __forceinline__ RowProg row_lane(uint32_t xs_v, int kind_v, int i) {
   RowProg r;
-  r.xs = p[i].xs;
-  r.z = p[i].z;
+  r.xs = (uint32_t)__builtin_amdgcn_readlane((int)xs_v, i);
+  r.z = (uint32_t)__builtin_amdgcn_readlane(kind_v, i);
   return r;
 }
 
@@ -885,10 +889,13 @@ __device__ __forceinline__ void append_field(uint32_t *out, int l, uint32_t (&wi
 // of the KDA variant, review "STEPQuant: When and Where Errors Matter in
 // Delta-Rule Recurrent State Quantization", Method).  Same thread mapping and
 // arithmetic as k_head.  Row widths are data, so:
-//   * each wave stages its half of the column streams in LDS; the per-row
-//     program (word offset, bit offset, width, completing shift) is read
-//     with scalar loads and used directly as instruction operands, so no
-//     per-row scalar arithmetic runs;
+//   * each wave stages its half of the column streams in LDS; lane l holds
+//     the program of row l of the half (word offset | bit offset, width,
+//     completing shift) in vector registers, loaded once with the codes, and
+//     each row's entry is broadcast with v_readlane into scalar registers
+//     that serve directly as instruction operands.  (Scalar loads of the
+//     tables inside the loops would share the LDS wait counter, so every LDS
+//     wait there would also wait for a table load from L2.);
 //   * R1 restores every row as an integer row (a funnel shift of two words,
 //     then one sign-extending extract of the row's width), straight-line;
 //     rows stored as FP16/FP32 pivots are redone in uniform branches (R2)
@@ -960,25 +967,42 @@ k_rows(const LaunchArgs P) {
   uint32_t *codes = lds_codes + (size_t)w * P.region_rows * kDim;   // [word][column]
   uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
   const uint32_t lane_byte = (uint32_t)l * 4u;                       // column l of word 0
-  // this half's rows, read through the constant address space: the tables
-  // never change during a launch, so every read is a scalar load (batched
-  // by the compiler) even after the kernel has stored
-  const const_rowprog_t uprog = (const_rowprog_t)(P.row_unpack + (size_t)h * kDim + 64 * w);
-  const const_rowprog_t pprog = (const_rowprog_t)(P.row_pack + (size_t)h * kDim + 64 * w);
+  // this half's row programs: lane l loads row 64w + l's entries
+  const RowProg *uprog = P.row_unpack + (size_t)h * kDim + 64 * w;
+  const RowProg *pprog = P.row_pack + (size_t)h * kDim + 64 * w;
+  const uint32_t uxs_v = uprog[l].xs, pxs_v = pprog[l].xs;
+  const int my_kind = (int)uprog[l].z;
+  // the row's readout weight, loaded with the rest of the row data
+  const float omega_row = dual(SCALE) ? (P.omega + (size_t)h * kDim)[row] : 1.0f;
 
   float S[2][64];
   float colc[2] = {1.0f, 1.0f};
 
-  // ---------------- stage this half's code words in LDS (1 KiB per wave instruction)
+  // ---------------- stage this half's code words in LDS (1 KiB per wave
+  // instruction).  The chunk count is data, so the loads are issued eight at
+  // a time, unconditionally, ahead of their LDS writes: a loop of load, wait,
+  // write would pay one memory round trip per chunk.  Lanes past the end of
+  // the half (and chunks past the last) take an offset beyond the buffer's
+  // range, which reads zeros without a memory access (so a last chunk of one
+  // word row also zeroes the spare row).
   if (restores(MODE)) {
-    for (uint32_t boff = (uint32_t)l * 16u; boff < half_bytes; boff += 1024u)
-      *reinterpret_cast<uint4 *>(codes8 + boff) = load_granule(rs, boff, half_off);
+    const uint32_t nchunks = (half_bytes + 1023u) >> 10;
+    for (uint32_t g0 = 0; g0 < nchunks; g0 += 8u) {
+      uint4 t[8];
+#pragma unroll
+      for (uint32_t u = 0; u < 8u; ++u) {
+        const uint32_t boff = (g0 + u) * 1024u + (uint32_t)l * 16u;
+        t[u] = load_granule(rs, boff < half_bytes ? boff : kBeyondBuffer, half_off);
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < 8u; ++u)
+        if (g0 + u < nchunks) *reinterpret_cast<uint4 *>(codes8 + (g0 + u) * 1024u + (uint32_t)l * 16u) = t[u];
+    }
     codes[nwords * kDim + l] = 0u;
     codes[nwords * kDim + 64 + l] = 0u;
   }
 
   // ---------------- per-row scalars of this lane's row
-  const int my_kind = (int)uprog[l].z;
   const bool my_int = my_kind <= 8;
   const float my_q = my_int ? (float)((1 << (my_kind - 1)) - 1) : 0.0f;
   // rows of this half stored as FP16/FP32 pivots, and as FP32 (bit ii = row 64w+ii)
@@ -1023,7 +1047,7 @@ k_rows(const LaunchArgs P) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 4 * i4 + e;
-        const RowProg pr = row_op(uprog, ii);
+        const RowProg pr = row_lane(uxs_v, my_kind, ii);
         const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -1033,10 +1057,16 @@ k_rows(const LaunchArgs P) {
       }
           }
     if (pivots != 0) {
+      // pivot rows are rare: test eight rows at a time, then the rows of a
+      // group that holds any
 #pragma unroll
-      for (int ii = 0; ii < 64; ++ii) {
-        if ((pivots >> ii) & 1u) {
-          const RowProg pr = row_op(uprog, ii);
+      for (int g8 = 0; g8 < 8; ++g8) {
+        if (((pivots >> (8 * g8)) & 0xFFu) == 0u) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ii = 8 * g8 + e;
+          if (!((pivots >> ii) & 1u)) continue;
+          const RowProg pr = row_lane(uxs_v, my_kind, ii);
           const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
           const float gi = sh.g[64 * w + ii];
 #pragma unroll
@@ -1127,7 +1157,7 @@ k_rows(const LaunchArgs P) {
   float r_row = 0.0f, m_row = 0.0f;
   if (dual(SCALE)) {
     m_row = row_reduce<false>(S, red, l) * 0.0078125f;
-    const float nu = rn_div(m_row, (P.omega + (size_t)h * kDim)[row]);
+    const float nu = rn_div(m_row, omega_row);
     r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
   } else {
     const float mx = row_reduce<true>(S, red, l);
@@ -1135,20 +1165,39 @@ k_rows(const LaunchArgs P) {
   }
   if constexpr (SC16) r_row = bf16_up(r_row);
   if (!my_int) { r_row = 0.0f; m_row = 0.0f; }
-  // pivot rows keep their values through the Y pass (factor 1) and are
-  // excluded from the column maximum (flag 0)
-  sh.ir[row] = my_int ? rn_div(1.0f, r_row) : 1.0f;
+  // Pivot rows leave their stored bits (fp16 or fp32 of S) in LDS now (the
+  // row reduction's scratch is free), so the Y pass can zero them (factor 0):
+  // they add nothing to the column maximum or the refit sums, and their code
+  // bits are replaced by the stash afterwards.
+  uint32_t *stash = codes;   // [pivot rank][column]
+  if (pivots != 0) {
+#pragma unroll
+    for (int g8 = 0; g8 < 8; ++g8) {
+      if (((pivots >> (8 * g8)) & 0xFFu) == 0u) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ii = 8 * g8 + e;
+        if (!((pivots >> ii) & 1u)) continue;
+        const bool f32row = (fp32_rows >> ii) & 1u;
+        const int rank = __builtin_popcountll(pivots & ((1ull << ii) - 1ull));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          stash[rank * 128 + l + 64 * c] = f32row ? __float_as_uint(S[c][ii])
+                                                  : (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])));
+      }
+    }
+  }
+  sh.ir[row] = my_int ? rn_div(1.0f, r_row) : 0.0f;
   sh.m[row] = m_row;
   __builtin_amdgcn_wave_barrier();
 
-  // Y = S / r in place (integer rows), and the column maximum over integer rows
+  // Y = S / r in place (integer rows; pivot rows become 0), and the column
+  // maximum, to which only integer rows contribute
   float cm[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int i4 = 0; i4 < 16; ++i4) {
     const float4 r4 = lds4(&sh.ir[64 * w + 4 * i4]);
-    const float4 q4 = lds4(&sh.qm[64 * w + 4 * i4]);
     const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-    const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ii = 4 * i4 + e;
@@ -1156,12 +1205,10 @@ k_rows(const LaunchArgs P) {
       for (int c = 0; c < 2; ++c) {
         const float y = S[c][ii] * rr[e];
         S[c][ii] = y;
-        // qm is 0 exactly for pivot rows: max(cm, |y| * 0) leaves cm unchanged
-        // (|y| is finite for finite states), so no branch is needed
-        cm[c] = fmaxf(cm[c], (qq[e] > 0.0f) ? fabsf(y) : 0.0f);
+        cm[c] = fmaxf(cm[c], fabsf(y));
       }
     }
-      }
+  }
   float c0[2] = {1.0f, 1.0f};
   if (dual(SCALE)) {
     sh.cmax[w][l] = cm[0];
@@ -1185,20 +1232,6 @@ k_rows(const LaunchArgs P) {
   // or fp32 of S) in LDS; P1 turns every value into its code bits in place
   // (straight-line); P2 appends each row's field to the column windows in
   // row order and stores every completed word.
-  uint32_t *stash = codes;   // [pivot rank][column] (free after the row reduction)
-  if (pivots != 0) {
-#pragma unroll
-    for (int ii = 0; ii < 64; ++ii) {
-      if ((pivots >> ii) & 1u) {
-        const uint32_t kind = uprog[ii].z;
-        const int rank = __builtin_popcountll(pivots & ((1ull << ii) - 1ull));
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          stash[rank * 128 + l + 64 * c] = (kind == 16u) ? (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])))
-                                                       : __float_as_uint(S[c][ii]);
-      }
-    }
-  }
   // V1a refit sums: fma chains over the integer rows in ascending order, so
   // wave 1 starts from wave 0's totals over rows 0..63 (it waits for them)
   float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
@@ -1241,10 +1274,13 @@ k_rows(const LaunchArgs P) {
   }
   if (pivots != 0) {
     // pivot rows: their stored bits replace the code bits
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int ii = 0; ii < 64; ++ii) {
-      if ((pivots >> ii) & 1u) {
+    for (int g8 = 0; g8 < 8; ++g8) {
+      if (((pivots >> (8 * g8)) & 0xFFu) == 0u) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ii = 8 * g8 + e;
+        if (!((pivots >> ii) & 1u)) continue;
         const int rank = __builtin_popcountll(pivots & ((1ull << ii) - 1ull));
         T[0][ii] = stash[rank * 128 + l];
         T[1][ii] = stash[rank * 128 + l + 64];
@@ -1262,7 +1298,7 @@ k_rows(const LaunchArgs P) {
       // completes it (or by the final flush), later in program order.
 #pragma unroll
       for (int ii = 0; ii < 64; ++ii) {
-        const RowProg pr = row_op(pprog, ii);
+        const RowProg pr = row_lane(pxs_v, my_kind, ii);
         uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
         o[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], pr.xs);
         o[64] = __builtin_amdgcn_alignbit(T[1][ii], win[1], pr.xs);
@@ -1272,7 +1308,7 @@ k_rows(const LaunchArgs P) {
     } else {
 #pragma unroll
       for (int ii = 0; ii < 64; ++ii) {
-        const RowProg pr = row_op(uprog, ii);
+        const RowProg pr = row_lane(uxs_v, my_kind, ii);
         const uint32_t off = ((pr.xs & ~511u) >> 4) + (pr.xs & 31u);   // stream bit of the field in this half
         if (pr.z == 32u) {   // an FP32 row: its two 16-bit halves in turn
           append_field(codes, l, win, T[0][ii], T[1][ii], off, 16u);
@@ -1284,7 +1320,7 @@ k_rows(const LaunchArgs P) {
     }
     // a partly filled last word: its bits sit at the top of the window;
     // shift them down with zeros above (the padding of the half)
-    const RowProg plast = row_op(uprog, 63);
+    const RowProg plast = row_lane(uxs_v, my_kind, 63);
     const uint32_t end = ((plast.xs & ~511u) >> 4) + (plast.xs & 31u) + plast.z;
     const uint32_t rem = end & 31u;
     if (rem != 0u) {
@@ -1293,8 +1329,19 @@ k_rows(const LaunchArgs P) {
       o[64] = __builtin_amdgcn_alignbit(0u, win[1], 32u - rem);
     }
     __builtin_amdgcn_wave_barrier();
-    for (uint32_t boff = (uint32_t)l * 16u; boff < half_bytes; boff += 1024u)
-      store_granule(rs, *reinterpret_cast<const uint4 *>(codes8 + boff), boff, half_off);
+    // eight LDS reads ahead of their stores, as in the staging
+    const uint32_t nchunks = (half_bytes + 1023u) >> 10;
+    for (uint32_t g0 = 0; g0 < nchunks; g0 += 8u) {
+      uint4 t[8];
+#pragma unroll
+      for (uint32_t u = 0; u < 8u; ++u)
+        if (g0 + u < nchunks) t[u] = *reinterpret_cast<const uint4 *>(codes8 + (g0 + u) * 1024u + (uint32_t)l * 16u);
+#pragma unroll
+      for (uint32_t u = 0; u < 8u; ++u) {
+        const uint32_t boff = (g0 + u) * 1024u + (uint32_t)l * 16u;
+        if (g0 + u < nchunks && boff < half_bytes) store_granule(rs, t[u], boff, half_off);
+      }
+    }
   }
 
   // ---------------- row and column factors (stored after every read of the

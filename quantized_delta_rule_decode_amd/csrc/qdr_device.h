@@ -528,6 +528,9 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       }
     }
   }
+  // the row's readout weight, loaded with the rest of the item (a load at
+  // its use, after the restore, would add a memory round trip)
+  const float omega_row = (INT && dual(SCALE)) ? (P.omega + (size_t)h * kDim)[row] : 1.0f;
 
   // ---------------- per-row scalars of this lane's row, broadcast via LDS
   float a_row = 1.0f;
@@ -646,7 +649,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     float r_row, m_row = 0.0f;
     if (dual(SCALE)) {
       m_row = row_reduce<false>(S, sh.red[w], l) * 0.0078125f;
-      const float nu = rn_div(m_row, (P.omega + (size_t)h * kDim)[row]);
+      const float nu = rn_div(m_row, omega_row);
       r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
     } else {
       const float mx = row_reduce<true>(S, sh.red[w], l);
@@ -967,27 +970,77 @@ k_rows(const LaunchArgs P) {
   uint32_t *codes = lds_codes + (size_t)w * P.region_rows * kDim;   // [word][column]
   uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
   const uint32_t lane_byte = (uint32_t)l * 4u;                       // column l of word 0
+  // ---------------- every load of the item goes out here, ahead of the
+  // first wait: the row programs and row data, then the code chunks (the HBM
+  // stream).  (Loads issued after a wait, or behind a branch on loaded data,
+  // would each add a memory round trip.)
   // this half's row programs: lane l loads row 64w + l's entries
   const RowProg *uprog = P.row_unpack + (size_t)h * kDim + 64 * w;
   const RowProg *pprog = P.row_pack + (size_t)h * kDim + 64 * w;
   const uint32_t uxs_v = uprog[l].xs, pxs_v = pprog[l].xs;
   const int my_kind = (int)uprog[l].z;
-  // the row's readout weight, loaded with the rest of the row data
   const float omega_row = dual(SCALE) ? (P.omega + (size_t)h * kDim)[row] : 1.0f;
-
-  float S[2][64];
+  float a_row = 1.0f;
+  if (has_readout(MODE)) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
+  // factors: r of every row (pivot rows' entries are read and ignored), c of
+  // the lane's two columns; a head without integer rows stores none
+  float r_raw = 1.0f;
   float colc[2] = {1.0f, 1.0f};
-
-  // ---------------- stage this half's code words in LDS (1 KiB per wave
-  // instruction).  The chunk count is data, so the loads are issued eight at
-  // a time, unconditionally, ahead of their LDS writes: a loop of load, wait,
-  // write would pay one memory round trip per chunk.  Lanes past the end of
-  // the half (and chunks past the last) take an offset beyond the buffer's
-  // range, which reads zeros without a memory access (so a last chunk of one
-  // word row also zeroes the spare row).
+  if (restores(MODE) && has_int) {
+    r_raw = load_sc<SC16>(rs, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
+    if (dual(SCALE)) {
+      colc[0] = load_sc<SC16>(rs, (uint32_t)l, c_off);
+      colc[1] = load_sc<SC16>(rs, (uint32_t)l + 64u, c_off);
+    }
+  }
+  float vcol[2] = {0.0f, 0.0f};
+  float kr = 0.0f, qr = 0.0f, beta_b = 0.0f;
+  if (has_readout(MODE)) {
+    load_qkv<io16(MODE)>(P, bh, row, l, kr, qr, vcol);
+    beta_b = P.beta[bh];
+  }
+  // code chunks of this half (1 KiB per wave instruction), the first eight
+  // unconditionally: lanes past the end of the half, and chunks past the
+  // last, take an offset beyond the buffer's range, which reads zeros
+  // without a memory access (so a last chunk of one word row also zeroes the
+  // spare row)
+  const uint32_t nchunks = (half_bytes + 1023u) >> 10;
+  uint4 chunk[8];
   if (restores(MODE)) {
-    const uint32_t nchunks = (half_bytes + 1023u) >> 10;
-    for (uint32_t g0 = 0; g0 < nchunks; g0 += 8u) {
+#pragma unroll
+    for (uint32_t u = 0; u < 8u; ++u) {
+      const uint32_t boff = u * 1024u + (uint32_t)l * 16u;
+      chunk[u] = load_granule(rs, boff < half_bytes ? boff : kBeyondBuffer, half_off);
+    }
+  }
+  // keep the scheduler from hoisting a use of the loaded data (and its wait)
+  // above the loads
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---------------- per-row scalars of this lane's row
+  const bool my_int = my_kind <= 8;
+  const float my_q = my_int ? (float)((1 << (my_kind - 1)) - 1) : 0.0f;
+  // rows of this half stored as FP16/FP32 pivots, and as FP32 (bit ii = row 64w+ii)
+  const uint64_t pivots = __ballot(!my_int);
+  const uint64_t fp32_rows = __ballot(my_kind == 32);
+  sh.qm[row] = my_q;
+  if (FIT) sh.iq[row] = my_int ? rn_div(1.0f, my_q) : 0.0f;
+  if (restores(MODE)) sh.g[row] = my_int ? a_row * rn_div(r_raw, my_q) : a_row;
+  if (has_readout(MODE)) {
+    sh.k[row] = kr;
+    sh.b[row] = beta_b * kr;
+    sh.q[row] = qr;
+  }
+
+  // ---------------- stage the code words in LDS: the first eight chunks
+  // from registers, any further ones (halves over 8 KiB) in batches of eight
+  // loads ahead of their writes
+  float S[2][64];
+  if (restores(MODE)) {
+#pragma unroll
+    for (uint32_t u = 0; u < 8u; ++u)
+      if (u < nchunks) *reinterpret_cast<uint4 *>(codes8 + u * 1024u + (uint32_t)l * 16u) = chunk[u];
+    for (uint32_t g0 = 8u; g0 < nchunks; g0 += 8u) {
       uint4 t[8];
 #pragma unroll
       for (uint32_t u = 0; u < 8u; ++u) {
@@ -1000,37 +1053,6 @@ k_rows(const LaunchArgs P) {
     }
     codes[nwords * kDim + l] = 0u;
     codes[nwords * kDim + 64 + l] = 0u;
-  }
-
-  // ---------------- per-row scalars of this lane's row
-  const bool my_int = my_kind <= 8;
-  const float my_q = my_int ? (float)((1 << (my_kind - 1)) - 1) : 0.0f;
-  // rows of this half stored as FP16/FP32 pivots, and as FP32 (bit ii = row 64w+ii)
-  const uint64_t pivots = __ballot(!my_int);
-  const uint64_t fp32_rows = __ballot(my_kind == 32);
-  sh.qm[row] = my_q;
-  if (FIT) sh.iq[row] = my_int ? rn_div(1.0f, my_q) : 0.0f;
-  float a_row = 1.0f;
-  if (has_readout(MODE)) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
-  if (restores(MODE)) {
-    if (my_int) {
-      const float r_row = load_sc<SC16>(rs, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
-      sh.g[row] = a_row * rn_div(r_row, my_q);
-    } else {
-      sh.g[row] = a_row;
-    }
-    if (dual(SCALE) && has_int) {
-      colc[0] = load_sc<SC16>(rs, (uint32_t)l, c_off);
-      colc[1] = load_sc<SC16>(rs, (uint32_t)l + 64u, c_off);
-    }
-  }
-  float vcol[2] = {0.0f, 0.0f};
-  if (has_readout(MODE)) {
-    float kr, qr;
-    load_qkv<io16(MODE)>(P, bh, row, l, kr, qr, vcol);
-    sh.k[row] = kr;
-    sh.b[row] = P.beta[bh] * kr;
-    sh.q[row] = qr;
   }
   __builtin_amdgcn_wave_barrier();
 

@@ -857,15 +857,16 @@ k_head_int(const LaunchArgs P) {
   else head_body<2, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
 }
 
-// Row i's program entry, broadcast from lane i of the per-lane table
-// registers (i is a compile-time lane index, so each field is one v_readlane
-// into a scalar register).
-__device__ __forceinline__ RowProg row_lane(uint32_t xs_v, int kind_v, int i) {
-  RowProg r;
-  r.xs = (uint32_t)__builtin_amdgcn_readlane((int)xs_v, i);
-  r.z = (uint32_t)__builtin_amdgcn_readlane(kind_v, i);
-  return r;
+// Row i's program word, broadcast from lane i of the per-lane table register
+// (i is a compile-time lane index: one v_readlane into a scalar register).
+__device__ __forceinline__ uint32_t row_lane(uint32_t xs_v, int i) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)xs_v, i);
 }
+// fields of a program word: LDS byte offset of the field's first word, the
+// width of a 2..16-bit field, the repack's completing shift (low 5 bits)
+__device__ __forceinline__ uint32_t rp_base(uint32_t e) { return e & ~511u; }
+__device__ __forceinline__ uint32_t rp_width(uint32_t e) { return (e >> 4) & 30u; }
+__device__ __forceinline__ uint32_t rp_pack_shift(uint32_t e) { return 0u - e; }
 
 // Append one field of `kind` bits (1..16) at stream bit `off` of a
 // column-half stream to the two column windows of a lane.  A window holds
@@ -893,10 +894,10 @@ __device__ __forceinline__ void append_field(uint32_t *out, int l, uint32_t (&wi
 // Delta-Rule Recurrent State Quantization", Method).  Same thread mapping and
 // arithmetic as k_head.  Row widths are data, so:
 //   * each wave stages its half of the column streams in LDS; lane l holds
-//     the program of row l of the half (word offset | bit offset, width,
-//     completing shift) in vector registers, loaded once with the codes, and
-//     each row's entry is broadcast with v_readlane into scalar registers
-//     that serve directly as instruction operands.  (Scalar loads of the
+//     the program word of row l of the half (word offset | width code | bit
+//     offset) in a vector register, loaded once with the codes, and each
+//     row's word is broadcast with v_readlane into a scalar register whose
+//     fields serve as instruction operands.  (Scalar loads of the
 //     tables inside the loops would share the LDS wait counter, so every LDS
 //     wait there would also wait for a table load from L2.);
 //   * R1 restores every row as an integer row (a funnel shift of two words,
@@ -975,10 +976,9 @@ k_rows(const LaunchArgs P) {
   // stream).  (Loads issued after a wait, or behind a branch on loaded data,
   // would each add a memory round trip.)
   // this half's row programs: lane l loads row 64w + l's entries
-  const RowProg *uprog = P.row_unpack + (size_t)h * kDim + 64 * w;
-  const RowProg *pprog = P.row_pack + (size_t)h * kDim + 64 * w;
-  const uint32_t uxs_v = uprog[l].xs, pxs_v = pprog[l].xs;
-  const int my_kind = (int)uprog[l].z;
+  const RowProg *prog = P.row_prog + (size_t)h * kDim + 64 * w;
+  const uint32_t xs_v = prog[l].xs;
+  const int my_kind = (int)prog[l].z;
   const float omega_row = dual(SCALE) ? (P.omega + (size_t)h * kDim)[row] : 1.0f;
   float a_row = 1.0f;
   if (has_readout(MODE)) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
@@ -1069,11 +1069,12 @@ k_rows(const LaunchArgs P) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 4 * i4 + e;
-        const RowProg pr = row_lane(uxs_v, my_kind, ii);
-        const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
+        const uint32_t pe = row_lane(xs_v, ii);
+        const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const int32_t z = sext_low(__builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pr.xs), pr.z);
+          // FP32 rows have width 0 here (and give 0); R2 redoes them
+          const int32_t z = sext_low(__builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pe), rp_width(pe));
           S[c][ii] = ((float)z * gg[e]) * colc[c];
         }
       }
@@ -1088,14 +1089,15 @@ k_rows(const LaunchArgs P) {
         for (int e = 0; e < 8; ++e) {
           const int ii = 8 * g8 + e;
           if (!((pivots >> ii) & 1u)) continue;
-          const RowProg pr = row_lane(uxs_v, my_kind, ii);
-          const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
+          const uint32_t pe = row_lane(xs_v, ii);
+          const bool f32row = (fp32_rows >> ii) & 1u;
+          const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
           const float gi = sh.g[64 * w + ii];
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const uint32_t f = __builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pr.xs);
-            S[c][ii] = gi * (pr.z == 16u ? __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu)))
-                                         : __uint_as_float(f));
+            const uint32_t f = __builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pe);
+            S[c][ii] = gi * (f32row ? __uint_as_float(f)
+                                    : __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu))));
           }
         }
       }
@@ -1320,30 +1322,30 @@ k_rows(const LaunchArgs P) {
       // completes it (or by the final flush), later in program order.
 #pragma unroll
       for (int ii = 0; ii < 64; ++ii) {
-        const RowProg pr = row_lane(pxs_v, my_kind, ii);
-        uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + ((pr.xs & ~511u) | lane_byte));
-        o[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], pr.xs);
-        o[64] = __builtin_amdgcn_alignbit(T[1][ii], win[1], pr.xs);
-        win[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], pr.z);
-        win[1] = __builtin_amdgcn_alignbit(T[1][ii], win[1], pr.z);
+        const uint32_t pe = row_lane(xs_v, ii);
+        uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
+        o[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_pack_shift(pe));
+        o[64] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_pack_shift(pe));
+        win[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_width(pe));
+        win[1] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_width(pe));
       }
     } else {
 #pragma unroll
       for (int ii = 0; ii < 64; ++ii) {
-        const RowProg pr = row_lane(uxs_v, my_kind, ii);
-        const uint32_t off = ((pr.xs & ~511u) >> 4) + (pr.xs & 31u);   // stream bit of the field in this half
-        if (pr.z == 32u) {   // an FP32 row: its two 16-bit halves in turn
+        const uint32_t pe = row_lane(xs_v, ii);
+        const uint32_t off = (rp_base(pe) >> 4) + (pe & 31u);   // stream bit of the field in this half
+        if ((fp32_rows >> ii) & 1u) {   // an FP32 row: its two 16-bit halves in turn
           append_field(codes, l, win, T[0][ii], T[1][ii], off, 16u);
           append_field(codes, l, win, T[0][ii] >> 16, T[1][ii] >> 16, off + 16u, 16u);
         } else {
-          append_field(codes, l, win, T[0][ii], T[1][ii], off, pr.z);
+          append_field(codes, l, win, T[0][ii], T[1][ii], off, rp_width(pe));
         }
       }
     }
     // a partly filled last word: its bits sit at the top of the window;
     // shift them down with zeros above (the padding of the half)
-    const RowProg plast = row_lane(uxs_v, my_kind, 63);
-    const uint32_t end = ((plast.xs & ~511u) >> 4) + (plast.xs & 31u) + plast.z;
+    const uint32_t plast = row_lane(xs_v, 63);
+    const uint32_t end = (rp_base(plast) >> 4) + (plast & 31u) + (((fp32_rows >> 63) & 1u) ? 32u : rp_width(plast));
     const uint32_t rem = end & 31u;
     if (rem != 0u) {
       uint32_t *o = codes + (end >> 5) * kDim + l;

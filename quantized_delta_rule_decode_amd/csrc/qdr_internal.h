@@ -33,19 +33,20 @@ struct ListEntry {
 };
 static_assert(sizeof(HeadInfo) == 16 && sizeof(ListEntry) == 32, "device table layout");
 
-// Row units: two tables with one entry per (head, row) describing the row's
-// field in its half of the column streams, as operands the kernel uses
-// directly (each entry is one 8-byte scalar load; no per-row scalar
-// arithmetic runs on the device).  With x = byte offset of the field's first
+// Row units: a table with one entry per (head, row) describing the row's
+// field in its half of the column streams, as operands the kernel uses with
+// at most two scalar instructions each.  With x = byte offset of the field's first
 // 32-bit word in the half's [word][column] image (word index * 512, so its
 // low 9 bits are zero), y = bit offset of the field in that word and
-// z = the field's width (the row's kind):
-//   unpack entry: {x | y, z}            (restore: funnel shift by y)
-//   pack entry:   {x | ((32 - y) & 31), z}  (repack: completing shift)
-// A funnel shift reads only the low 5 bits of its shift operand, and the
-// LDS address is (x | y) with the low 9 bits replaced by the lane's byte.
+// z = the field's width (the row's kind).  One word serves the restore and
+// the repack:
+//   xs = x | (z / 2) << 5 | y   (z / 2 in 1..8 for the 2..16-bit kinds, 0 for FP32)
+// The restore's funnel shift by y and the repack's completing shift by
+// (32 - y) & 31 = (-xs) & 31 read only the low 5 bits of their operand;
+// (xs >> 4) & 30 is the width of a 2..16-bit field; the LDS address is x
+// with the low 9 bits replaced by the lane's byte.
 struct RowProg {
-  uint32_t xs;   // x | shift
+  uint32_t xs;   // x | width code | shift
   uint32_t z;    // width
 };
 
@@ -57,8 +58,7 @@ struct LaunchArgs {
   int32_t H;
   const ListEntry *head_list;   // heads handled by this launch
   int32_t n_list;
-  const RowProg *row_unpack;  // [H*128] (row units)
-  const RowProg *row_pack;    // [H*128] (row units)
+  const RowProg *row_prog;    // [H*128] (row units)
   int32_t region_rows;        // row units: LDS rows of 128 words in each wave's region
   const float *omega;         // [H*128]
   uint32_t *err;              // device error word

@@ -63,7 +63,7 @@ struct HostLayout {
   std::vector<uint64_t> head_off;
   std::vector<uint32_t> head_bytes, code_bytes;
   std::vector<uint8_t> words0, words1; // row units: words per column and half
-  std::vector<qdr::RowProg> row_unpack, row_pack;  // row units: [H*128] each
+  std::vector<qdr::RowProg> row_prog;  // row units: [H*128]
   std::vector<uint8_t> has_scales;
   uint64_t slot_stride = 0;
   int max_words = 0;
@@ -116,8 +116,7 @@ void build_layout(const qdr_pool_desc *d, HostLayout &L) {
   L.words1.resize(H);
   L.has_scales.resize(H);
   if (d->unit == QDR_UNIT_ROW) {
-    L.row_unpack.resize((size_t)H * QDR_DIM);
-    L.row_pack.resize((size_t)H * QDR_DIM);
+    L.row_prog.resize((size_t)H * QDR_DIM);
   }
   uint64_t off = 0;
   double bits = 0;
@@ -134,8 +133,8 @@ void build_layout(const qdr_pool_desc *d, HostLayout &L) {
         const int k = d->unit == QDR_UNIT_HEAD ? d->kinds[h] : d->kinds[(size_t)h * QDR_DIM + i];
         if (d->unit == QDR_UNIT_ROW) {
           const uint32_t x = (uint32_t)(hbits >> 5) * (QDR_DIM * 4u), y = (uint32_t)(hbits & 31u);
-          L.row_unpack[(size_t)h * QDR_DIM + i] = {x | y, (uint32_t)k};
-          L.row_pack[(size_t)h * QDR_DIM + i] = {x | ((32u - y) & 31u), (uint32_t)k};
+          const uint32_t wcode = k == 32 ? 0u : (uint32_t)k / 2u;
+          L.row_prog[(size_t)h * QDR_DIM + i] = {x | (wcode << 5) | y, (uint32_t)k};
         }
         hbits += (uint64_t)k;
         any_int = any_int || is_int_kind(k);
@@ -174,7 +173,7 @@ struct qdr_pool {
   int device = 0;
   uint8_t *base = nullptr;
   bool owns_base = false;
-  qdr::RowProg *d_row_unpack = nullptr, *d_row_pack = nullptr;
+  qdr::RowProg *d_row_prog = nullptr;
   float *d_omega = nullptr;
   uint32_t *d_err = nullptr;
   qdr::ListEntry *d_lists[qdr::kNumLists] = {};
@@ -218,8 +217,7 @@ std::vector<qdr::ListEntry> interleave_int_heads(const std::vector<std::vector<q
 void free_pool(qdr_pool *p) {
   if (!p) return;
   if (p->owns_base && p->base) (void)hipFree(p->base);
-  (void)hipFree(p->d_row_unpack);
-  (void)hipFree(p->d_row_pack);
+  (void)hipFree(p->d_row_prog);
   (void)hipFree(p->d_omega);
   (void)hipFree(p->d_err);
   for (auto &l : p->d_lists) (void)hipFree(l);
@@ -233,8 +231,7 @@ qdr::LaunchArgs base_args(const qdr_pool *p) {
   a.slot_stride = p->L.slot_stride;
   a.num_slots = p->desc.num_slots;
   a.H = p->desc.num_heads;
-  a.row_unpack = p->d_row_unpack;
-  a.row_pack = p->d_row_pack;
+  a.row_prog = p->d_row_prog;
   a.omega = p->d_omega;
   a.err = p->d_err;
   return a;
@@ -347,8 +344,7 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
   hipError_t e = hipMemset(p->base, 0, total);
   if (e == hipSuccess) e = upload(&p->d_omega, p->omega.data(), p->omega.size());
   if (e == hipSuccess && desc->unit == QDR_UNIT_ROW) {
-    e = upload(&p->d_row_unpack, p->L.row_unpack.data(), p->L.row_unpack.size());
-    if (e == hipSuccess) e = upload(&p->d_row_pack, p->L.row_pack.data(), p->L.row_pack.size());
+    e = upload(&p->d_row_prog, p->L.row_prog.data(), p->L.row_prog.size());
   }
   for (int i = 0; i < qdr::kNumLists && e == hipSuccess; ++i) {
     p->list_count[i] = (int32_t)lists[i].size();

@@ -528,33 +528,33 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       }
     }
   }
-  // the row's readout weight, loaded with the rest of the item (a load at
-  // its use, after the restore, would add a memory round trip)
+  // the rest of the item's loads, all issued before the first wait: the
+  // row's readout weight (a load at its use, after the restore, would add a
+  // memory round trip), the gate, the factors, q/k/v and beta
   const float omega_row = (INT && dual(SCALE)) ? (P.omega + (size_t)h * kDim)[row] : 1.0f;
-
-  // ---------------- per-row scalars of this lane's row, broadcast via LDS
   float a_row = 1.0f;
-  if (has_readout(MODE)) {
-    a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
-  }
-  if (restores(MODE)) {
-    if (INT) {
-      const float r_row = load_sc<SC16>(rs, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
-      sh.g[row] = (a_row * rn_div(r_row, QMAX)) * GSCALE;
-      if (dual(SCALE)) {
-        colc[0] = load_sc<SC16>(rs, (uint32_t)l, c_off);
-        colc[1] = load_sc<SC16>(rs, (uint32_t)l + 64u, c_off);
-      }
-    } else {
-      sh.g[row] = a_row;
+  if (has_readout(MODE)) a_row = (GATE == 0) ? P.gate[bh] : (P.gate + bh * kDim)[row];
+  float r_raw = 1.0f;
+  if (restores(MODE) && INT) {
+    r_raw = load_sc<SC16>(rs, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
+    if (dual(SCALE)) {
+      colc[0] = load_sc<SC16>(rs, (uint32_t)l, c_off);
+      colc[1] = load_sc<SC16>(rs, (uint32_t)l + 64u, c_off);
     }
   }
   float vcol[2] = {0.0f, 0.0f};
+  float kr = 0.0f, qr = 0.0f, beta_b = 0.0f;
   if (has_readout(MODE)) {
-    float kr, qr;
     load_qkv<io16(MODE)>(P, bh, row, l, kr, qr, vcol);
+    beta_b = P.beta[bh];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---------------- per-row scalars of this lane's row, broadcast via LDS
+  if (restores(MODE)) sh.g[row] = INT ? (a_row * rn_div(r_raw, QMAX)) * GSCALE : a_row;
+  if (has_readout(MODE)) {
     sh.k[row] = kr;
-    sh.b[row] = P.beta[bh] * kr;
+    sh.b[row] = beta_b * kr;
     sh.q[row] = qr;
   }
   __builtin_amdgcn_wave_barrier();

@@ -1030,7 +1030,11 @@ k_rows(const LaunchArgs P) {
     sh.k[row] = kr;
     sh.b[row] = beta_b * kr;
     sh.q[row] = qr;
+    // v waits in the delta slots (wave 1 forms delta there) and omega in the
+    // 1/r slot (overwritten by 1/r), so neither holds a register meanwhile
+    if (w == 1) { sh.d[l] = vcol[0]; sh.d[l + 64] = vcol[1]; }
   }
+  if (dual(SCALE)) sh.ir[row] = omega_row;
 
   // ---------------- stage the code words in LDS: the first eight chunks
   // from registers, any further ones (halves over 8 KiB) in batches of eight
@@ -1139,27 +1143,27 @@ k_rows(const LaunchArgs P) {
     if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
     chain_rows(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
     if (w == 1) {
-      sh.d[l] = vcol[0] - acc2[0];
-      sh.d[l + 64] = vcol[1] - acc2[1];
-      oq[0] = acc1[0]; oq[1] = acc1[1];
+      sh.d[l] = sh.d[l] - acc2[0];
+      sh.d[l + 64] = sh.d[l + 64] - acc2[1];
+      // wave 1's readout part goes where wave 0's u part was (already read)
+      sh.x[l] = acc1[0];
+      sh.x[l + 64] = acc1[1];
     } else {
       oq[0] = acc2[0]; oq[1] = acc2[1];
     }
     __syncthreads();
     dl[0] = sh.d[l];
     dl[1] = sh.d[l + 64];
-    if constexpr (MODE == MODE_READOUT) {
-      // readout-first launch: o = S'^T q + (q . b) delta as in the step;
-      // the state is neither updated nor stored (the write-back launch does it)
-      if (w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
-      __syncthreads();
-      if (w == 0 && P.o != nullptr) {
-        const float qb_all = sh.qb[0] + sh.qb[1];
-        out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
-        out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
-      }
-      return;
+    // the readout, o = S'^T q + (q . b) delta (tolerance-checked, any
+    // summation order), written as soon as delta is known
+    if (writes_o(MODE) && w == 0 && P.o != nullptr) {
+      const float qb_all = sh.qb[0] + sh.qb[1];
+      out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
+      out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
     }
+    // readout-first launch: the state is neither updated nor stored (the
+    // write-back launch does it)
+    if constexpr (MODE == MODE_READOUT) return;
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
@@ -1181,7 +1185,7 @@ k_rows(const LaunchArgs P) {
   float r_row = 0.0f, m_row = 0.0f;
   if (dual(SCALE)) {
     m_row = row_reduce<false>(S, red, l) * 0.0078125f;
-    const float nu = rn_div(m_row, omega_row);
+    const float nu = rn_div(m_row, sh.ir[row]);   // omega of the row
     r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
   } else {
     const float mx = row_reduce<true>(S, red, l);
@@ -1213,6 +1217,9 @@ k_rows(const LaunchArgs P) {
   }
   sh.ir[row] = my_int ? rn_div(1.0f, r_row) : 0.0f;
   sh.m[row] = m_row;
+  // factors are stored as soon as they are known (every read of the block
+  // was issued and waited for before the restore)
+  if (has_int) store_sc<SC16>(rs, r_row, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
   __builtin_amdgcn_wave_barrier();
 
   // Y = S / r in place (integer rows; pivot rows become 0), and the column
@@ -1238,7 +1245,6 @@ k_rows(const LaunchArgs P) {
     sh.cmax[w][l] = cm[0];
     sh.cmax[w][l + 64] = cm[1];
   }
-  if (is_step(MODE) && w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
   __syncthreads();
   if (dual(SCALE)) {
 #pragma unroll
@@ -1251,6 +1257,10 @@ k_rows(const LaunchArgs P) {
   float ec[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) ec[c] = dual(SCALE) ? rn_div(1.0f, c0[c]) : 1.0f;
+  if (dual(SCALE) && has_int && !FIT && w == 0) {
+    store_sc<SC16>(rs, c0[0], (uint32_t)l, c_off);
+    store_sc<SC16>(rs, c0[1], (uint32_t)l + 64u, c_off);
+  }
 
   // ---------------- codes.  Pivot rows first leave their stored bits (fp16
   // or fp32 of S) in LDS; P1 turns every value into its code bits in place
@@ -1368,16 +1378,9 @@ k_rows(const LaunchArgs P) {
     }
   }
 
-  // ---------------- row and column factors (stored after every read of the
-  // row tables, so those stay scalar loads)
-  if (has_int) store_sc<SC16>(rs, r_row, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
-  if (dual(SCALE) && has_int) {
-    if (!FIT) {
-      if (w == 0) {
-        store_sc<SC16>(rs, c0[0], (uint32_t)l, c_off);
-        store_sc<SC16>(rs, c0[1], (uint32_t)l + 64u, c_off);
-      }
-    } else if (w == 1) {
+  // ---------------- refitted column factors
+  if (FIT && dual(SCALE) && has_int) {
+    if (w == 1) {
       // wave 1 holds the sums over all integer rows
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -1388,12 +1391,6 @@ k_rows(const LaunchArgs P) {
     }
   }
 
-  // ---------------- readout
-  if (writes_o(MODE) && w == 0 && P.o != nullptr) {
-    const float qb_all = sh.qb[0] + sh.qb[1];
-    out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
-    out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
-  }
 }
 
 // --------------------------------------------------------------------------

@@ -1,12 +1,12 @@
 // qdr_dispatch.cpp -- picks the kernels of one mode: the row-unit kernel, or
 // for whole-head pools one launch over every integer head (kinds mixed) and
-// one launch per float kind present, back to back on the stream.
+// one launch per float kind present.
 #include "qdr_internal.h"
 
 namespace qdr {
 
 hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const ListEntry *const *kind_lists,
-                      const int32_t *kind_counts, int mode, hipStream_t stream) {
+                      const int32_t *kind_counts, int mode, hipStream_t stream, hipStream_t float_stream) {
   if (n <= 0) return hipSuccess;
   if (cfg.unit != 0) return launch_rows_mode(cfg, args, n, kind_lists[0], kind_counts[0], mode, stream);
   hipError_t e = hipSuccess;
@@ -26,12 +26,12 @@ hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n, const ListE
   if (e == hipSuccess && kind_counts[4] > 0) {
     args.head_list = kind_lists[4];
     args.n_list = kind_counts[4];
-    e = launch_head_b16(cfg, args, n, mode, stream);
+    e = launch_head_b16(cfg, args, n, mode, float_stream);
   }
   if (e == hipSuccess && kind_counts[5] > 0) {
     args.head_list = kind_lists[5];
     args.n_list = kind_counts[5];
-    e = launch_head_b32(cfg, args, n, mode, stream);
+    e = launch_head_b32(cfg, args, n, mode, float_stream);
   }
   return e;
 }

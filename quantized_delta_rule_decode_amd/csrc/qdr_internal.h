@@ -99,10 +99,12 @@ hipError_t launch_rows_mode(const PoolConfig &, const LaunchArgs &, int n, const
 constexpr int kNumLists = 7;
 constexpr int kListIntMix = 6;
 
-// Launch every kernel of one mode over `n` requests / dense entries.
-// Returns hipSuccess or the first launch error.
+// Launch the kernels of one mode over `n` requests / dense entries: the
+// row-unit kernel, or for whole-head pools the integer launch on `stream`
+// and the float-kind launches on `float_stream` (the caller orders the two
+// streams).  Returns hipSuccess or the first launch error.
 hipError_t launch_all(const PoolConfig &cfg, LaunchArgs args, int n,
                       const ListEntry *const *kind_lists, const int32_t *kind_counts,
-                      int mode, hipStream_t stream);
+                      int mode, hipStream_t stream, hipStream_t float_stream);
 
 }  // namespace qdr

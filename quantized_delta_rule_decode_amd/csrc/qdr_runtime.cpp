@@ -182,6 +182,11 @@ struct qdr_pool {
   // every later call on the pool orders its stream after it
   hipEvent_t wb_done = nullptr;
   bool wb_recorded = false;
+  // whole-head pools with integer and float heads: the float-kind launches
+  // run on a stream of the pool's own, forked from and joined back to the
+  // caller's stream by two events, so they overlap the integer launch
+  hipStream_t float_stream = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
 };
 
 namespace {
@@ -222,6 +227,9 @@ void free_pool(qdr_pool *p) {
   (void)hipFree(p->d_err);
   for (auto &l : p->d_lists) (void)hipFree(l);
   if (p->wb_done) (void)hipEventDestroy(p->wb_done);
+  if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
+  if (p->join_ev) (void)hipEventDestroy(p->join_ev);
+  if (p->float_stream) (void)hipStreamDestroy(p->float_stream);
   delete p;
 }
 
@@ -267,7 +275,18 @@ qdr_status dispatch(qdr_pool *p, qdr::LaunchArgs a, int n, int mode, hipStream_t
   if (we != hipSuccess) return fail(QDR_E_DEVICE, "stream wait failed: %s", hipGetErrorString(we));
   const qdr::ListEntry *lists[qdr::kNumLists];
   for (int i = 0; i < qdr::kNumLists; ++i) lists[i] = p->d_lists[i];
-  hipError_t e = qdr::launch_all(p->cfg, a, n, lists, p->list_count, mode, st);
+  hipError_t e;
+  if (p->float_stream && n > 0) {
+    // fork: the float stream starts after everything before this call on
+    // st; join: st continues after the float launches
+    e = hipEventRecord(p->fork_ev, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(p->float_stream, p->fork_ev, 0);
+    if (e == hipSuccess) e = qdr::launch_all(p->cfg, a, n, lists, p->list_count, mode, st, p->float_stream);
+    if (e == hipSuccess) e = hipEventRecord(p->join_ev, p->float_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, p->join_ev, 0);
+  } else {
+    e = qdr::launch_all(p->cfg, a, n, lists, p->list_count, mode, st, st);
+  }
   if (e == hipErrorNotSupported) return fail(QDR_E_UNSUPPORTED, "this pool configuration has no kernel");
   if (e != hipSuccess) return fail(QDR_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -349,6 +368,13 @@ qdr_status qdr_pool_create(const qdr_pool_desc *desc, void *dev_mem, size_t dev_
   for (int i = 0; i < qdr::kNumLists && e == hipSuccess; ++i) {
     p->list_count[i] = (int32_t)lists[i].size();
     e = upload(&p->d_lists[i], lists[i].data(), lists[i].size());
+  }
+  const bool has_int_heads = p->list_count[qdr::kListIntMix] > 0;
+  const bool has_float_heads = desc->unit == QDR_UNIT_HEAD && (p->list_count[4] > 0 || p->list_count[5] > 0);
+  if (e == hipSuccess && has_int_heads && has_float_heads) {
+    e = hipStreamCreateWithFlags(&p->float_stream, hipStreamNonBlocking);   // default priority
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->join_ev, hipEventDisableTiming);
   }
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&p->d_err), sizeof(uint32_t));
   if (e == hipSuccess) e = hipMemset(p->d_err, 0, sizeof(uint32_t));

@@ -254,7 +254,8 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--fp32-warmup-steps", type=int, default=None,
                     help="FP32 delta-rule steps that build the warm state (default: the config's)")
-    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--cpu-requests", type=int, default=64,
+                    help="requests in the oracle's timed sample (64 x 2304 heads: about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-comparator", action="store_true",
                     help="skip timing the FP32-state pool of the warm-up")
@@ -363,9 +364,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "unit_of_work": ("one qdr_decode_step: whole-head pools launch k_head_int over every "
-                                      "integer head (the dominant kernel) plus one launch per float kind, "
-                                      "back to back on one stream; row-unit pools launch k_rows once; "
-                                      "achieved = algorithmic bytes per step / step time"),
+                                      "integer head (the dominant kernel) and, on a second stream forked "
+                                      "from and joined back to the caller's, one launch per float kind; "
+                                      "row-unit pools launch k_rows once; achieved = algorithmic bytes per "
+                                      "step / step time (HIP events on the caller's stream)"),
                      "traffic_over_algorithmic": None if traffic is None else traffic / nbytes,
                      "stream_reference": stream,
                      "frac_of_stream_reference": achieved / stream["GBps"]},

@@ -278,8 +278,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 3}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step has no "
-              "cross-GPU term, see the sharding paragraph of DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode step has no "
+              "cross-GPU term; heads or requests would shard across GPUs without communication",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

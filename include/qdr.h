@@ -18,11 +18,19 @@
  * Conventions for every entry point:
  *   - Tensor pointers (q, k, v, beta, gate, o, S, slots) are DEVICE pointers
  *     to contiguous arrays, 4-byte aligned, owned by the caller; the library
- *     never frees or retains them past the call.
+ *     never frees them, and they must stay valid (and the inputs unchanged)
+ *     until the work the call enqueues on `stream` has completed.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is
  *     enqueued asynchronously and the call returns without synchronising,
  *     except where stated (read_raw, write_raw, poll_device_error, and the
- *     host-side slot check enabled by QDR_DEBUG=1).
+ *     host-side slot check enabled by QDR_DEBUG=1).  A whole-head pool that
+ *     holds FP16 or FP32 heads next to integer heads also launches on a
+ *     stream of its own (default priority, created with the pool): that work
+ *     is forked from `stream` by an event recorded there and joined back by
+ *     an event `stream` waits on, so work enqueued on `stream` after the call
+ *     sees all of its results.  Fork and join are event operations, so a
+ *     call on a capturing stream is captured whole into a HIP graph.  Calls
+ *     on one pool from several host threads at once race.
  *   - Every call returns a qdr_status.  Argument errors are found on the host
  *     before anything is enqueued, so a failed call has no side effects.
  *     qdr_last_error() gives a message for the calling thread.  No C++

@@ -187,7 +187,7 @@ __device__ __forceinline__ uint4 load_granule(rsrc_t rs, uint32_t voff, uint32_t
 
 __device__ __forceinline__ void store_granule(rsrc_t rs, uint4 t, uint32_t voff, uint32_t soff) {
   __attribute__((ext_vector_type(4))) unsigned int v = {t.x, t.y, t.z, t.w};
-  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, 2);   // nontemporal: written once per step
 }
 
 __device__ __forceinline__ float load_f32(rsrc_t rs, uint32_t voff, uint32_t soff) {

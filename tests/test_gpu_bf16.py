@@ -38,8 +38,9 @@ def round_bf16(x):
 CASES = [("head", "with_pivots", 0), ("head", "int_all", 1), ("head", "fp32", 0), ("row", "kda_mix", 1)]
 
 
+@pytest.mark.parametrize("sb", [32, 16])
 @pytest.mark.parametrize("unit,name,gate", CASES)
-def test_bf16_step_parity(torch_dev, orc, unit, name, gate):
+def test_bf16_step_parity(torch_dev, orc, unit, name, gate, sb):
     torch = torch_dev
     if unit == "head":
         kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
@@ -49,8 +50,8 @@ def test_bf16_step_parity(torch_dev, orc, unit, name, gate):
         kinds = row_kinds(name, H, 7)
         fp16 = kinds.reshape(H, D) == 16
     omega = np.random.default_rng(3).lognormal(0, 1, (H, D)).astype(np.float32)
-    dev, ref = make_pair(orc, 6, kinds, omega, unit=u, gate=gate)
-    twin = qdr.Pool(6, H, kinds, omega, unit=u, gate=gate)     # fp32-I/O step on the widened inputs
+    dev, ref = make_pair(orc, 6, kinds, omega, unit=u, gate=gate, sb=sb)
+    twin = qdr.Pool(6, H, kinds, omega, unit=u, gate=gate, scale_bits=sb)   # fp32-I/O step on the widened inputs
     S = edge_states(23, 6, H, fp16)
     all_slots = np.arange(6, dtype=np.int32)
     for p in (dev, twin):
@@ -58,7 +59,7 @@ def test_bf16_step_parity(torch_dev, orc, unit, name, gate):
     ref.pack(all_slots, S)
     slots = np.array([4, -1, 0, 5, 2], np.int32)
     for step in range(2):
-        print(f"bf16 {unit} {name} gate={gate} step {step}", flush=True)
+        print(f"bf16 {unit} {name} gate={gate} sb={sb} step {step}", flush=True)
         q, k, v, beta, g = random_inputs(50 + step, slots.size, H, gate == 1)
         q16, k16, v16 = (round_bf16(x) for x in (q, k, v))
         wq, wk, wv = (widen(x) for x in (q16, k16, v16))
@@ -79,7 +80,7 @@ def test_bf16_step_parity(torch_dev, orc, unit, name, gate):
         # oracle: blocks as in the fp32 parity tests, o within one bfloat16 rounding
         rep = parity.StepReport()
         parity.compare_pool(orc, ref, dev, slots, parity.step_state_fn(orc, ref, prev, slots, inputs), rep)
-        parity.assert_step_ok(rep, f"bf16 {unit} {name} gate={gate} step {step}")
+        parity.assert_step_ok(rep, f"bf16 {unit} {name} gate={gate} sb={sb} step {step}")
         o_dev = widen(o_dev16)
         assert np.all(np.abs(o_dev - o_ref) <= 2.0 ** -8 * np.abs(o_ref) + 1e-38)
         assert np.linalg.norm(o_dev - o_ref) <= 2.0 ** -8 * np.linalg.norm(o_ref)

@@ -45,8 +45,9 @@ CASES = [("head", name, gate) for name in sorted(HEAD_KIND_SETS) for gate in (0,
         [("row", "kda_mix", 1), ("row", "fp32_rows", 0)]
 
 
+@pytest.mark.parametrize("sb", [32, 16])
 @pytest.mark.parametrize("unit,name,gate", CASES)
-def test_split_step_parity(torch_dev, orc, unit, name, gate):
+def test_split_step_parity(torch_dev, orc, unit, name, gate, sb):
     torch = torch_dev
     if unit == "head":
         kinds = np.array(HEAD_KIND_SETS[name], np.uint8)
@@ -57,7 +58,7 @@ def test_split_step_parity(torch_dev, orc, unit, name, gate):
         kinds = row_kinds(name, H, 7)
         fp16 = kinds.reshape(H, D) == 16
     omega = np.random.default_rng(3).lognormal(0, 1, (H, D)).astype(np.float32)
-    dev, ref = make_pair(orc, 6, kinds, omega, unit=u, gate=gate)
+    dev, ref = make_pair(orc, 6, kinds, omega, unit=u, gate=gate, sb=sb)
     S = edge_states(21, 6, H, fp16)
     all_slots = np.arange(6, dtype=np.int32)
     dev.qdr_pack(t_(torch, all_slots), t_(torch, S))
@@ -65,18 +66,19 @@ def test_split_step_parity(torch_dev, orc, unit, name, gate):
     sr, sw = torch.cuda.Stream(), torch.cuda.Stream()
     slots = np.array([4, -1, 0, 5, 2], np.int32)
     for step in range(2):
-        print(f"split {unit} {name} gate={gate} step {step}", flush=True)
+        print(f"split {unit} {name} gate={gate} sb={sb} step {step}", flush=True)
         inputs = random_inputs(30 + step, slots.size, H, gate == 1)
         rep, o_dev, bad = split_step_pair(torch, orc, dev, ref, slots, inputs, sr, sw)
-        parity.assert_step_ok(rep, f"split {unit} {name} gate={gate} step {step}")
+        parity.assert_step_ok(rep, f"split {unit} {name} gate={gate} sb={sb} step {step}")
         assert bad == 0 and np.all(o_dev[1] == 0)
     for s in (1, 3):   # untouched slots keep their bytes
         assert np.array_equal(dev.qdr_read_raw(s), ref.mem[s * ref.slot_stride:(s + 1) * ref.slot_stride])
     assert dev.qdr_poll_device_error() == 0
 
 
+@pytest.mark.parametrize("sb", [32, 16])
 @pytest.mark.parametrize("unit", ["head", "row"])
-def test_split_equals_fused_without_host_sync(torch_dev, unit):
+def test_split_equals_fused_without_host_sync(torch_dev, unit, sb):
     torch = torch_dev
     if unit == "head":
         kinds = np.array([16, 8, 6, 4, 2, 6, 8, 32], np.uint8)
@@ -88,8 +90,8 @@ def test_split_equals_fused_without_host_sync(torch_dev, unit):
         fp16 = kinds.reshape(H, D) == 16
     omega = np.random.default_rng(4).lognormal(0, 1, (H, D)).astype(np.float32)
     gate = 1 if unit == "row" else 0
-    fused = qdr.Pool(8, H, kinds, omega, unit=u, gate=gate)
-    split = qdr.Pool(8, H, kinds, omega, unit=u, gate=gate)
+    fused = qdr.Pool(8, H, kinds, omega, unit=u, gate=gate, scale_bits=sb)
+    split = qdr.Pool(8, H, kinds, omega, unit=u, gate=gate, scale_bits=sb)
     S = t_(torch, edge_states(22, 8, H, fp16))
     all_slots = t_(torch, np.arange(8, dtype=np.int32))
     fused.qdr_pack(all_slots, S)

@@ -362,6 +362,36 @@ __device__ __forceinline__ void chain_rows(const float (&S)[2][64], float (&acc)
   }
 }
 
+// Calls f(i4, x4) on the 16 float4 groups of a 64-entry per-row LDS table in
+// order, each group's read issued A groups before its use (the row-unit
+// kernel runs two waves per SIMD, too few to cover an LDS read issued one
+// group ahead).
+template <int A, class F>
+__device__ __forceinline__ void row_groups(const float *t, F &&f) {
+  float4 q[16];
+#pragma unroll
+  for (int g = 0; g < A; ++g) q[g] = lds4(t + 4 * g);
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    if (g + A < 16) q[g + A] = lds4(t + 4 * (g + A));
+    f(g, q[g]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// chain_rows with its table reads issued ahead (row_groups)
+__device__ __forceinline__ void chain_rows_ahead(const float (&S)[2][64], float (&acc)[2], const float *xsh,
+                                                 int row0) {
+  row_groups<4>(xsh + row0, [&](int i4, const float4 x4) {
+    const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[0] = __builtin_fmaf(xx[e], S[0][4 * i4 + e], acc[0]);
+      acc[1] = __builtin_fmaf(xx[e], S[1][4 * i4 + e], acc[1]);
+    }
+  });
+}
+
 // DPP row move of x (dpp_ctrl CTRL, all rows and banks enabled).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -1066,23 +1096,34 @@ k_rows(const LaunchArgs P) {
   // in row order.
   float acc1[2] = {0.0f, 0.0f};
   if (restores(MODE)) {
+    // the staged words of row ii + kAhead are read while row ii is restored,
+    // so a row's LDS reads have kAhead rows of work to land in (read in the
+    // row's turn, each row would wait out its own LDS latency)
+    constexpr int kAhead = 4;
+    uint32_t pe_q[64], wq[64][4];
+    float4 gq[16];
+    auto fetch = [&](int ii) {
+      pe_q[ii] = row_lane(xs_v, ii);
+      const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + (rp_base(pe_q[ii]) | lane_byte));
+      wq[ii][0] = wp[0]; wq[ii][1] = wp[64]; wq[ii][2] = wp[kDim]; wq[ii][3] = wp[kDim + 64];
+      if ((ii & 3) == 0) gq[ii >> 2] = lds4(&sh.g[64 * w + ii]);
+    };
 #pragma unroll
-    for (int i4 = 0; i4 < 16; ++i4) {
-      const float4 g4 = lds4(&sh.g[64 * w + 4 * i4]);
-      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+    for (int ii = 0; ii < kAhead; ++ii) fetch(ii);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ii = 4 * i4 + e;
-        const uint32_t pe = row_lane(xs_v, ii);
-        const uint32_t *wp = reinterpret_cast<const uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
+    for (int ii = 0; ii < 64; ++ii) {
+      const float4 g4 = gq[ii >> 2];
+      const float gi = ((ii & 3) == 0) ? g4.x : ((ii & 3) == 1) ? g4.y : ((ii & 3) == 2) ? g4.z : g4.w;
+      const uint32_t pe = pe_q[ii];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          // FP32 rows have width 0 here (and give 0); R2 redoes them
-          const int32_t z = sext_low(__builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pe), rp_width(pe));
-          S[c][ii] = ((float)z * gg[e]) * colc[c];
-        }
+      for (int c = 0; c < 2; ++c) {
+        // FP32 rows have width 0 here (and give 0); R2 redoes them
+        const int32_t z = sext_low(__builtin_amdgcn_alignbit(wq[ii][2 + c], wq[ii][c], pe), rp_width(pe));
+        S[c][ii] = ((float)z * gi) * colc[c];
       }
-          }
+      if (ii + kAhead < 64) fetch(ii + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (pivots != 0) {
       // pivot rows are rare: test eight rows at a time, then the rows of a
       // group that holds any
@@ -1106,7 +1147,7 @@ k_rows(const LaunchArgs P) {
         }
       }
     }
-    if (has_readout(MODE)) chain_rows(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
+    if (has_readout(MODE)) chain_rows_ahead(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
   }
 
   if (MODE == MODE_UNPACK) {
@@ -1141,7 +1182,7 @@ k_rows(const LaunchArgs P) {
     __syncthreads();
     float acc2[2] = {0.0f, 0.0f};
     if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
-    chain_rows(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
+    chain_rows_ahead(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
     if (w == 1) {
       sh.d[l] = sh.d[l] - acc2[0];
       sh.d[l + 64] = sh.d[l + 64] - acc2[1];
@@ -1164,9 +1205,7 @@ k_rows(const LaunchArgs P) {
     // readout-first launch: the state is neither updated nor stored (the
     // write-back launch does it)
     if constexpr (MODE == MODE_READOUT) return;
-#pragma unroll
-    for (int i4 = 0; i4 < 16; ++i4) {
-      const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
+    row_groups<4>(&sh.b[64 * w], [&](int i4, const float4 b4) {
       const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1174,7 +1213,7 @@ k_rows(const LaunchArgs P) {
         S[0][ii] = __builtin_fmaf(bb[e], dl[0], S[0][ii]);
         S[1][ii] = __builtin_fmaf(bb[e], dl[1], S[1][ii]);
       }
-          }
+    });
   }
 
 
@@ -1225,9 +1264,7 @@ k_rows(const LaunchArgs P) {
   // Y = S / r in place (integer rows; pivot rows become 0), and the column
   // maximum, to which only integer rows contribute
   float cm[2] = {0.0f, 0.0f};
-#pragma unroll
-  for (int i4 = 0; i4 < 16; ++i4) {
-    const float4 r4 = lds4(&sh.ir[64 * w + 4 * i4]);
+  row_groups<4>(&sh.ir[64 * w], [&](int i4, const float4 r4) {
     const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1239,7 +1276,7 @@ k_rows(const LaunchArgs P) {
         cm[c] = fmaxf(cm[c], fabsf(y));
       }
     }
-  }
+  });
   float c0[2] = {1.0f, 1.0f};
   if (dual(SCALE)) {
     sh.cmax[w][l] = cm[0];
@@ -1275,9 +1312,7 @@ k_rows(const LaunchArgs P) {
     dacc[0] = sh.y[l]; dacc[1] = sh.y[l + 64];
   }
   uint32_t (&T)[2][64] = reinterpret_cast<uint32_t (&)[2][64]>(S);   // code bits, in place
-#pragma unroll
-  for (int i4 = 0; i4 < 16; ++i4) {
-    const float4 q4 = lds4(&sh.qm[64 * w + 4 * i4]);
+  row_groups<4>(&sh.qm[64 * w], [&](int i4, const float4 q4) {
     const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
     float4 m4 = {0, 0, 0, 0}, iq4 = {0, 0, 0, 0};
     if (FIT) { m4 = lds4(&sh.m[64 * w + 4 * i4]); iq4 = lds4(&sh.iq[64 * w + 4 * i4]); }
@@ -1300,7 +1335,7 @@ k_rows(const LaunchArgs P) {
         T[c][ii] = __float_as_uint(t);
       }
     }
-      }
+  });
   if (FIT && dual(SCALE) && w == 0) {
     sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
     sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];

@@ -379,10 +379,11 @@ __device__ __forceinline__ void row_groups(const float *t, F &&f) {
   }
 }
 
-// chain_rows with its table reads issued ahead (row_groups)
+// chain_rows with its table reads issued A groups ahead (row_groups)
+template <int A>
 __device__ __forceinline__ void chain_rows_ahead(const float (&S)[2][64], float (&acc)[2], const float *xsh,
                                                  int row0) {
-  row_groups<4>(xsh + row0, [&](int i4, const float4 x4) {
+  row_groups<A>(xsh + row0, [&](int i4, const float4 x4) {
     const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1001,6 +1002,9 @@ k_rows(const LaunchArgs P) {
   uint32_t *codes = lds_codes + (size_t)w * P.region_rows * kDim;   // [word][column]
   uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
   const uint32_t lane_byte = (uint32_t)l * 4u;                       // column l of word 0
+  // rows (restore) and table groups (other passes) whose LDS reads are in
+  // flight ahead of their use; the refit's extra sums leave room for two
+  constexpr int kAhead = FIT ? 2 : 4;
   // ---------------- every load of the item goes out here, ahead of the
   // first wait: the row programs and row data, then the code chunks (the HBM
   // stream).  (Loads issued after a wait, or behind a branch on loaded data,
@@ -1099,7 +1103,6 @@ k_rows(const LaunchArgs P) {
     // the staged words of row ii + kAhead are read while row ii is restored,
     // so a row's LDS reads have kAhead rows of work to land in (read in the
     // row's turn, each row would wait out its own LDS latency)
-    constexpr int kAhead = 4;
     uint32_t pe_q[64], wq[64][4];
     float4 gq[16];
     auto fetch = [&](int ii) {
@@ -1147,7 +1150,7 @@ k_rows(const LaunchArgs P) {
         }
       }
     }
-    if (has_readout(MODE)) chain_rows_ahead(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
+    if (has_readout(MODE)) chain_rows_ahead<kAhead>(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
   }
 
   if (MODE == MODE_UNPACK) {
@@ -1182,7 +1185,7 @@ k_rows(const LaunchArgs P) {
     __syncthreads();
     float acc2[2] = {0.0f, 0.0f};
     if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
-    chain_rows_ahead(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
+    chain_rows_ahead<kAhead>(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
     if (w == 1) {
       sh.d[l] = sh.d[l] - acc2[0];
       sh.d[l + 64] = sh.d[l + 64] - acc2[1];
@@ -1205,7 +1208,7 @@ k_rows(const LaunchArgs P) {
     // readout-first launch: the state is neither updated nor stored (the
     // write-back launch does it)
     if constexpr (MODE == MODE_READOUT) return;
-    row_groups<4>(&sh.b[64 * w], [&](int i4, const float4 b4) {
+    row_groups<kAhead>(&sh.b[64 * w], [&](int i4, const float4 b4) {
       const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1264,7 +1267,7 @@ k_rows(const LaunchArgs P) {
   // Y = S / r in place (integer rows; pivot rows become 0), and the column
   // maximum, to which only integer rows contribute
   float cm[2] = {0.0f, 0.0f};
-  row_groups<4>(&sh.ir[64 * w], [&](int i4, const float4 r4) {
+  row_groups<kAhead>(&sh.ir[64 * w], [&](int i4, const float4 r4) {
     const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1312,7 +1315,7 @@ k_rows(const LaunchArgs P) {
     dacc[0] = sh.y[l]; dacc[1] = sh.y[l + 64];
   }
   uint32_t (&T)[2][64] = reinterpret_cast<uint32_t (&)[2][64]>(S);   // code bits, in place
-  row_groups<4>(&sh.qm[64 * w], [&](int i4, const float4 q4) {
+  row_groups<kAhead>(&sh.qm[64 * w], [&](int i4, const float4 q4) {
     const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
     float4 m4 = {0, 0, 0, 0}, iq4 = {0, 0, 0, 0};
     if (FIT) { m4 = lds4(&sh.m[64 * w + 4 * i4]); iq4 = lds4(&sh.iq[64 * w + 4 * i4]); }

@@ -1368,14 +1368,31 @@ k_rows(const LaunchArgs P) {
       // a field ends in is written whether or not the field completes it; a
       // word that is not yet complete is rewritten by the field that
       // completes it (or by the final flush), later in program order.
+      // this pass reads no LDS, so the program words come in by scalar loads
+      // (constant address space), eight rows per load, one batch ahead,
+      // instead of a v_readlane per row
+      typedef __attribute__((address_space(4))) const uint32_t cu32;
+      cu32 *pw = (cu32 *)(uintptr_t)prog;   // {xs, z} per row
+      uint32_t pb[2][8];
 #pragma unroll
-      for (int ii = 0; ii < 64; ++ii) {
-        const uint32_t pe = row_lane(xs_v, ii);
-        uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
-        o[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_pack_shift(pe));
-        o[64] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_pack_shift(pe));
-        win[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_width(pe));
-        win[1] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_width(pe));
+      for (int e = 0; e < 8; ++e) pb[0][e] = pw[2 * e];
+#pragma unroll
+      for (int b8 = 0; b8 < 8; ++b8) {
+        if (b8 + 1 < 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[(b8 + 1) & 1][e] = pw[2 * (8 * (b8 + 1) + e)];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ii = 8 * b8 + e;
+          const uint32_t pe = pb[b8 & 1][e];
+          uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
+          o[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_pack_shift(pe));
+          o[64] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_pack_shift(pe));
+          win[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_width(pe));
+          win[1] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_width(pe));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll

@@ -930,7 +930,9 @@ __device__ __forceinline__ void append_field(uint32_t *out, int l, uint32_t (&wi
 //     row's word is broadcast with v_readlane into a scalar register whose
 //     fields serve as instruction operands.  (Scalar loads of the
 //     tables inside the loops would share the LDS wait counter, so every LDS
-//     wait there would also wait for a table load from L2.);
+//     wait there would also wait for a table load from L2; only the
+//     repack's append pass, which reads no LDS, takes the words by scalar
+//     loads.);
 //   * R1 restores every row as an integer row (a funnel shift of two words,
 //     then one sign-extending extract of the row's width), straight-line;
 //     rows stored as FP16/FP32 pivots are redone in uniform branches (R2)

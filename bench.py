@@ -78,6 +78,47 @@ def cpu_baseline(cfg, tables, requests: int, threads: int):
     return requests * cfg.H / dt, dt
 
 
+def other_configs(cids=(1, 2, 3, 5), reps: int = 20):
+    """The other workloads' own figures: config 1 (one head) as latency per
+    step, configs 2 and 3 (cache-resident pools) as state-update steps/s,
+    config 5 (the (5B+1)-slot KDA pool, 38.7 GB) as steps/s, achieved GB/s of
+    its algorithmic bytes and the fraction of 8 TB/s.  Each pool starts from
+    its own initial state (config 1: 256 FP32 steps then pack; the others:
+    the zero state) and takes a few untimed steps before the timed ones; every
+    step is one qdr_decode_step on the same inputs."""
+    import torch
+    from quantized_delta_rule_decode_amd import synth, workload
+    out = {}
+    for cid in cids:
+        cfg = synth.CONFIGS[cid]
+        tables = synth.static_tables(cfg)
+        pool = workload.make_pool(cfg, tables)
+        slots = torch.from_numpy(tables["slots"]).cuda()
+        if cfg.warmup:
+            workload.warm_start(cfg, tables, pool, slots, cfg.warmup).close()
+        else:
+            pool.qdr_slot_reset(slots)
+        ins = workload.step_inputs(cfg, tables, 0)
+        o = torch.empty((cfg.B, cfg.H, 128), dtype=torch.float32, device="cuda")
+        ms = time_on_stream(lambda: pool.qdr_decode_step(slots, *ins, o), reps, warmup=5)
+        assert pool.qdr_poll_device_error() == 0
+        nbytes = algorithmic_bytes(cfg, tables)
+        rec = {"workload": cfg.name, "B": cfg.B, "heads": cfg.H, "ms_per_step": ms,
+               "state_update_steps_per_s": cfg.B * cfg.H / (ms * 1e-3),
+               "algorithmic_bytes_per_step": nbytes, "timed_steps": reps}
+        if cid == 1:
+            rec["latency_us_per_step"] = ms * 1e3
+        if cid == 5:
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            rec.update({"achieved_GBps": gbps, "frac_of_peak_hbm": gbps / PEAK_HBM_GBPS,
+                        "kernel": "k_rows (row units: per-key-row kinds)"})
+        out[f"config{cid}"] = rec
+        pool.close()
+        del pool
+        torch.cuda.synchronize()
+    return out
+
+
 def time_on_stream(fn, reps: int, warmup: int = 1) -> float:
     """Mean ms per call of fn() (device work on torch's current stream),
     HIP events recorded on that stream around `reps` calls."""
@@ -264,6 +305,10 @@ def main():
                          "bfloat16-scale pool")
     ap.add_argument("--no-trajectory-error", action="store_true",
                     help="skip the quantised-vs-FP32 trajectory error of the small configs")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing configs 1, 2, 3 and 5 next to the benchmark configuration")
+    ap.add_argument("--cpu-requests-single", type=int, default=2,
+                    help="requests in the single-threaded oracle sample (2 x 2304 heads: about 10 s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -336,12 +381,19 @@ def main():
     assert pool.qdr_poll_device_error() == 0
     stream = stream_reference()
     traj = None if args.no_trajectory_error else [fp32_trajectory_error(c) for c in (1, 2, 3)]
+    others = None if args.no_other_configs else other_configs()
     cpu = None
     if not args.no_cpu_baseline:
-        threads = min(os.cpu_count() or 1, 16)
+        host_cores = os.cpu_count() or 1
+        threads = min(host_cores, 16)
         rate, dt = cpu_baseline(cfg, tables, args.cpu_requests, threads)
+        rate1, dt1 = cpu_baseline(cfg, tables, args.cpu_requests_single, 1)
         cpu = {"value": rate, "unit": "state-update steps/s", "cores": threads, "kind": "oracle",
-               "sample": f"{args.cpu_requests} requests x {cfg.H} heads, one step ({dt:.2f} s)"}
+               "sample": f"{args.cpu_requests} requests x {cfg.H} heads, one step ({dt:.2f} s) on {threads} threads",
+               "host_cores": host_cores,
+               "single_thread": {"value": rate1, "unit": "state-update steps/s", "cores": 1,
+                                 "sample": f"{args.cpu_requests_single} requests x {cfg.H} heads, one step "
+                                           f"({dt1:.2f} s)"}}
 
     line = {
         "metric": METRIC,
@@ -378,6 +430,7 @@ def main():
         "bf16_io_step": bf16_io,
         "bf16_scales_step": sc16,
         "fp32_trajectory_error": traj,
+        "other_configs": others,
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "setup_s": setup_s,

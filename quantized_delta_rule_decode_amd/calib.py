@@ -162,6 +162,20 @@ def allocate(L, D, cand_bits, nominal, pivot_frac):
     return kinds, pivot
 
 
+def row_impact(q, k, beta, gate, head: bool):
+    """Coefficient of row i of the state stored before a step in that step's
+    readout: o_t = S_t^T q_t with S_t = A_t S_{t-1} + beta_t k_t v_t^T and
+    A_t = (I - beta_t k_t k_t^T) D_t, so d o_t / d S_{t-1}[i, j] = (A_t^T q_t)_i
+    for every column j, = d_i (q_i - beta k_i (k . q)) (Tutorial §三: a row's
+    impact is what an error stored in it contributes to the readout; Review
+    (singularity-lens), row paragraph: from the state-update transform and the
+    query).  q, k: [..., 128]; beta: [...]; gate: [...] (a scalar d per head,
+    head=True) or [..., 128] (diagonal d_i).  Torch tensors, any device."""
+    kq = (k * q).sum(dim=-1, keepdim=True)
+    coef = q - beta[..., None] * k * kq
+    return coef * (gate[..., None] if head else gate)
+
+
 def _steps(cc: CalibConfig, cfg, tables, T):
     from . import workload
     for t in range(T):
@@ -192,11 +206,7 @@ def calibrate(cc: CalibConfig, device: str = "cuda") -> dict:
         g64 = gate.double()
         ell_sum += g64.log().sum(dim=0)
         if t > 0:   # the state stored after step t-1 is read out through step t's transform
-            q64, k64 = q.double(), k.double()
-            kq = (k64 * q64).sum(dim=-1, keepdim=True)
-            coef = q64 - beta.double()[..., None] * k64 * kq
-            coef = coef * (g64[..., None] if head else g64)
-            om_sum += coef.square().sum(dim=0)
+            om_sum += row_impact(q.double(), k.double(), beta.double(), g64, head).square().sum(dim=0)
             n_om += B
         f32.qdr_decode_step(slots, q, k, v, beta, gate, o)
         if t + 1 in sample_at:

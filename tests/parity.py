@@ -19,6 +19,7 @@ D = 128
 TIE_WINDOW = 1e-6
 MAX_EXCUSED_FRACTION = 1e-4
 O_REL_L2 = 1e-4
+O_WORST_HEAD = 1e-3
 
 
 @dataclasses.dataclass
@@ -155,3 +156,19 @@ def assert_step_ok(rep: StepReport, what: str):
     assert rep.codes_excused <= MAX_EXCUSED_FRACTION * max(rep.codes_checked, 1), \
         f"{what}: {rep.codes_excused} excused codes of {rep.codes_checked}"
     assert rep.o_rel_l2 <= O_REL_L2, f"{what}: readout relative L2 {rep.o_rel_l2:.3e}"
+    assert rep.o_worst_head <= O_WORST_HEAD, f"{what}: worst head readout relative L2 {rep.o_worst_head:.3e}"
+
+
+def readout_row_sensitivity(orc, q, k, beta, a, eps=2.0 ** 12):
+    """d o_t / d S_{t-1}[i, j] (the same for every column j), measured through
+    the oracle's own decode step: an FP32-kind head whose stored state is
+    eps * I takes one step with v = 0, and its readout divided by eps is the
+    coefficient of each row (the step is linear in the stored state, and with
+    v = 0 the stored state is its only input).  a: the gate as a per-row
+    vector.  Returns float64 [128]."""
+    d = len(q)
+    S = (np.eye(d) * eps).astype(np.float32)
+    kinds = np.full(d, 32, np.uint8)
+    _, _, _, o, _ = orc.head_step(kinds, S.view(np.uint32), np.zeros(d, np.float32), np.ones(d, np.float32),
+                                  np.ones(d, np.float32), q, k, np.zeros(d, np.float32), float(beta), a)
+    return o.astype(np.float64) / eps

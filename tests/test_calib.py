@@ -86,3 +86,31 @@ def test_pivots_and_budget():
     assert kinds.astype(int).sum() > 6 * N - 4                       # and the budget is used
     with pytest.raises(ValueError):
         calib.allocate(L, D, bits, 4.05, 0.0139)                     # pivots + all-INT4 exceed it
+
+
+@pytest.mark.parametrize("head", [True, False])
+def test_row_impact_is_the_readout_sensitivity(orc, head):
+    """The row-impact coefficient equals the sensitivity of the next readout
+    to a row of the stored state, measured by perturbing the state through
+    the oracle's decode step (not by evaluating a formula)."""
+    import torch
+    import parity
+    g = np.random.default_rng(31 if head else 32)
+    B, H, D = 3, 4, 128
+    q = g.standard_normal((B, H, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True) * np.sqrt(D)
+    k = g.standard_normal((B, H, D))
+    k[..., :4] *= 8.0                                            # outlier key channels
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q[0, 0] = k[0, 0]                                            # a query along the key
+    q, k = q.astype(np.float32), k.astype(np.float32)
+    beta = g.uniform(0, 1, (B, H)).astype(np.float32)
+    beta[1, 1] = 1.0
+    gate = g.uniform(0.3, 1.0, (B, H) if head else (B, H, D)).astype(np.float32)
+    coef = calib.row_impact(*(torch.from_numpy(x).double() for x in (q, k, beta, gate)), head).numpy()
+    for b in range(B):
+        for h in range(H):
+            a = np.full(D, gate[b, h], np.float32) if head else gate[b, h]
+            fd = parity.readout_row_sensitivity(orc, q[b, h], k[b, h], beta[b, h], a)
+            scale = np.abs(a.astype(np.float64) * np.abs(q[b, h])).max() + np.abs(k[b, h]).max() * np.abs(q[b, h]).max()
+            assert np.max(np.abs(coef[b, h] - fd)) <= 1e-5 * scale, (b, h, np.max(np.abs(coef[b, h] - fd)) / scale)

@@ -12,8 +12,9 @@ from quantized_delta_rule_decode_amd import synth
 D = 128
 
 
-def ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c):
+def ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c, scale_bits=32):
     G = 16 if unit == 0 else 4
+    fb = 2 if scale_bits == 16 else 4          # bytes per stored factor
     widths = [int(k) for k in kinds]
     gbits = 8 * G
     ng0 = (sum(widths[:64]) + gbits - 1) // gbits
@@ -21,7 +22,7 @@ def ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c):
     ng = ng0 + ng1
     code_bytes = ng * D * G
     has_int = any(w <= 8 for w in widths)
-    sbytes = (2 * D * 4 if scale_mode == 0 else D * 4) if has_int else 0
+    sbytes = (2 * D * fb if scale_mode == 0 else D * fb) if has_int else 0
     size = (code_bytes + sbytes + 255) // 256 * 256
     out = bytearray(size)
     for j in range(D):
@@ -42,10 +43,17 @@ def ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c):
         raw = halves[0].to_bytes(ng0 * G, "little") + halves[1].to_bytes(ng1 * G, "little")
         for n, byte in enumerate(raw):
             out[((n // G) * D + j) * G + n % G] = byte
+    def factor_bytes(x):
+        u = np.asarray(x, np.float32).view(np.uint32)
+        if fb == 4:
+            return u.tobytes()
+        assert np.all(u & 0xFFFF == 0), "a 16-bit factor must be a bfloat16 value"
+        return b"".join(int(w >> 16).to_bytes(2, "little") for w in u)
+
     if has_int:
-        out[code_bytes:code_bytes + D * 4] = np.asarray(r, np.float32).tobytes()
+        out[code_bytes:code_bytes + D * fb] = factor_bytes(r)            # r right after the codes
         if scale_mode == 0:
-            out[code_bytes + D * 4:code_bytes + 2 * D * 4] = np.asarray(c, np.float32).tobytes()
+            out[code_bytes + D * fb:code_bytes + 2 * D * fb] = factor_bytes(c)   # then c
     return np.frombuffer(bytes(out), np.uint8)
 
 
@@ -82,19 +90,24 @@ KIND_SETS = {
 @pytest.mark.parametrize("name", sorted(KIND_SETS))
 @pytest.mark.parametrize("unit", [0, 1])
 @pytest.mark.parametrize("scale_mode", [0, 1])
-def test_encode_matches_reference_packer(orc, name, unit, scale_mode):
+@pytest.mark.parametrize("sb", [32, 16])
+def test_encode_matches_reference_packer(orc, name, unit, scale_mode, sb):
     kinds = np.array(KIND_SETS[name], np.uint8)
     if unit == 0 and len(set(kinds.tolist())) > 1:
         pytest.skip("whole-head units have one kind per head")
-    g = np.random.default_rng(hash((name, unit, scale_mode)) % 2 ** 32)
+    g = np.random.default_rng(hash((name, unit, scale_mode, sb)) % 2 ** 32)
     codes, fp_bits, e, r, c = random_head(g, kinds)
+    if sb == 16:
+        # bfloat16 factors: distinct random values whose low 16 bits are zero
+        r = (r.view(np.uint32) & 0xFFFF0000).view(np.float32)
+        c = (c.view(np.uint32) & 0xFFFF0000).view(np.float32)
     if not any(k <= 8 for k in kinds):
         r = np.zeros(D, np.float32)
-    blob = orc.encode_block(kinds, unit, scale_mode, e, r, c)
-    ref = ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c)
-    assert blob.size == ref.size == orc.block_bytes(kinds, unit, scale_mode)
+    blob = orc.encode_block(kinds, unit, scale_mode, e, r, c, scale_bits=sb)
+    ref = ref_pack(kinds, unit, scale_mode, codes, fp_bits, r, c, scale_bits=sb)
+    assert blob.size == ref.size == orc.block_bytes(kinds, unit, scale_mode, sb)
     assert np.array_equal(blob, ref)
-    e2, r2, c2 = orc.decode_block(kinds, unit, scale_mode, blob)
+    e2, r2, c2 = orc.decode_block(kinds, unit, scale_mode, blob, scale_bits=sb)
     assert np.array_equal(e2, e)
     if any(k <= 8 for k in kinds):
         assert np.array_equal(r2, r)

@@ -87,7 +87,8 @@ def _declare(L):
     L.or_pool_layout.argtypes = [ctypes.POINTER(PoolDesc), _p, _p, _p]
     L.or_pool_step.restype = ctypes.c_int
     L.or_pool_step.argtypes = [ctypes.POINTER(PoolDesc), _p, _p, ctypes.c_int32,
-                               _p, _p, _p, _p, _p, _p, ctypes.c_int]
+                               _p, _p, _p, _p, _p, _p, ctypes.c_int, _p]
+    L.or_readout_magnitude.argtypes = [ctypes.c_int, _p, _p, _p]
     L.or_pool_pack.restype = ctypes.c_int
     L.or_pool_pack.argtypes = [ctypes.POINTER(PoolDesc), _p, _p, ctypes.c_int32, _p,
                                ctypes.c_int]
@@ -146,6 +147,15 @@ def delta_update(Sp, k, v, beta):
     u = np.empty(d, np.float32)
     lib().or_delta_update(d, _ptr(Sp), _ptr(k), _ptr(v), ctypes.c_float(beta), _ptr(S), _ptr(u))
     return S, u
+
+
+def readout_magnitude(S, q):
+    S = _c(S, np.float32)
+    d = S.shape[0]
+    q = _c(q, np.float32)
+    m = np.empty(d, np.float32)
+    lib().or_readout_magnitude(d, _ptr(S), _ptr(q), _ptr(m))
+    return m
 
 
 def readout(S, q):
@@ -261,13 +271,16 @@ class Pool:
         return self.mem[off: off + self.block_size(h)]
 
     def step(self, slots, q, k, v, beta, gate, threads=1):
+        """One decode step of the listed slots; returns (o, number of bad
+        slots).  The readout magnitudes of the step are kept in last_o_mag."""
         slots = _c(slots, np.int32)
         B = slots.size
         q, k, v, beta, gate = (_c(x, np.float32) for x in (q, k, v, beta, gate))
         o = np.zeros((B, self.num_heads, 128), np.float32)
+        self.last_o_mag = np.zeros((B, self.num_heads, 128), np.float32)
         bad = lib().or_pool_step(ctypes.byref(self.desc), _ptr(self.mem), _ptr(slots), B,
                                  _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(o),
-                                 threads)
+                                 threads, _ptr(self.last_o_mag))
         return o, bad
 
     def pack(self, slots, S, threads=1):

@@ -166,6 +166,19 @@ void or_readout(int d, const float *S, const float *q, float *o) {
   }
 }
 
+/* Absolute scale of the readout: m_j = sum_i |q_i| |S_ij|, accumulated in   */
+/* double, then rounded.  Not part of the step: it is the scale of the       */
+/* rounding error of any evaluation order of o_j = sum_i q_i S_ij            */
+/* (|fl(x.y) - x.y| <= gamma_n |x|.|y|), which the checks of a readout that  */
+/* sums in another order need when the sum cancels.                          */
+void or_readout_magnitude(int d, const float *S, const float *q, float *m) {
+  for (int j = 0; j < d; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i) acc += fabs((double)q[i]) * fabs((double)S[i * d + j]);
+    m[j] = (float)acc;
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Steps a6-a8: refit the scales and quantise the updated state.             */
 /*                                                                           */
@@ -493,6 +506,7 @@ typedef struct {
   int32_t nreq;
   const float *q, *k, *v, *beta, *gate;
   float *o;
+  float *o_mag;            /* optional: readout magnitude per (b, h, j) */
   const float *S_in;
   float *S_out;
   int op;                  /* 0 step, 1 pack, 2 unpack */
@@ -516,6 +530,7 @@ static void run_items(work_t *w) {
     if (slot < 0 || slot >= desc->num_slots) {
       if (slot >= desc->num_slots || slot < -1) w->bad++;
       if (w->op == 0) memset(w->o + vec, 0, sizeof(float) * D128);
+      if (w->op == 0 && w->o_mag) memset(w->o_mag + vec, 0, sizeof(float) * D128);
       if (w->op == 2) memset(w->S_out + ((size_t)b * H + h) * nn, 0, sizeof(float) * nn);
       continue;
     }
@@ -528,7 +543,8 @@ static void run_items(work_t *w) {
         a[i] = desc->gate == OR_GATE_SCALAR ? w->gate[(size_t)b * H + h] : w->gate[vec + i];
       or_head_step(D128, kinds, e, r, c, omega, desc->scale_mode, desc->fit_iters, SB(desc),
                    w->q + vec, w->k + vec, w->v + vec, w->beta[(size_t)b * H + h], a,
-                   w->o + vec, NULL);
+                   w->o + vec, w->o_mag ? S : NULL);
+      if (w->o_mag) or_readout_magnitude(D128, S, w->q + vec, w->o_mag + vec);
       or_encode_block(kinds, desc->unit, desc->scale_mode, SB(desc), e, r, c, w->pool + boff);
     } else if (w->op == 1) {
       const float *omega = desc->omega + (size_t)h * D128;
@@ -583,11 +599,11 @@ static int run_pool(work_t *proto, int threads) {
 int or_pool_step(const or_pool_desc *desc, uint8_t *pool,
                  const int32_t *slots, int32_t B, const float *q,
                  const float *k, const float *v, const float *beta,
-                 const float *gate, float *o, int threads) {
+                 const float *gate, float *o, int threads, float *o_mag) {
   work_t w;
   memset(&w, 0, sizeof w);
   w.desc = desc; w.pool = pool; w.slots = slots; w.nreq = B;
-  w.q = q; w.k = k; w.v = v; w.beta = beta; w.gate = gate; w.o = o;
+  w.q = q; w.k = k; w.v = v; w.beta = beta; w.gate = gate; w.o = o; w.o_mag = o_mag;
   w.op = 0;
   return run_pool(&w, threads);
 }

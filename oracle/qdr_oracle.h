@@ -65,6 +65,9 @@ void or_dequant(int d, const uint8_t *kinds, const uint32_t *e,
 void or_delta_update(int d, const float *Sp, const float *k, const float *v,
                      float beta, float *S, float *u);
 void or_readout(int d, const float *S, const float *q, float *o);
+/* m_j = sum_i |q_i| |S_ij| (double accumulation): the error scale of any
+ * summation order of the readout, for checks only. */
+void or_readout_magnitude(int d, const float *S, const float *q, float *m);
 void or_requant(int d, const uint8_t *kinds, const float *S,
                 const float *omega, int scale_mode, int fit_iters,
                 int scale_bits, uint32_t *e, float *r, float *c,
@@ -110,11 +113,13 @@ int or_pool_layout(const or_pool_desc *desc, uint64_t *head_off,
 
 /* Step every (b, h) with slots[b] >= 0 in a host pool image.  Returns the
  * number of out-of-range slots (their o rows are zeroed; padding slots -1
- * also give zero o).  threads <= 1 runs on the calling thread. */
+ * also give zero o).  threads <= 1 runs on the calling thread.  o_mag
+ * (optional, may be NULL): [B][H][128] readout magnitudes
+ * (or_readout_magnitude of each updated state). */
 int or_pool_step(const or_pool_desc *desc, uint8_t *pool,
                  const int32_t *slots, int32_t B, const float *q,
                  const float *k, const float *v, const float *beta,
-                 const float *gate, float *o, int threads);
+                 const float *gate, float *o, int threads, float *o_mag);
 /* Encode dense fp32 states S[n][H][128][128] into the listed slots. */
 int or_pool_pack(const or_pool_desc *desc, uint8_t *pool,
                  const int32_t *slots, int32_t n, const float *S, int threads);

@@ -55,13 +55,14 @@ static int run_pool(int unit, int gate, int scale_mode, int fit, int scale_bits,
   const size_t nv = (size_t)B * H * D;
   float *q = malloc(sizeof(float) * nv), *k = malloc(sizeof(float) * nv), *v = malloc(sizeof(float) * nv);
   float *beta = malloc(sizeof(float) * B * H), *g = malloc(sizeof(float) * nv), *o = malloc(sizeof(float) * nv);
+  float *om = malloc(sizeof(float) * nv);
   int32_t slots[3] = {2, -1, 0};
   int steps = 0;
   for (int t = 0; t < 4; ++t) {
     for (size_t i = 0; i < nv; ++i) { q[i] = normal() * 0.1f; k[i] = normal() * 0.09f; v[i] = normal(); g[i] = 0.5f + 0.5f * uniform(); }
     for (int i = 0; i < B * H; ++i) beta[i] = uniform();
     if (t == 3) slots[1] = 9;                            /* an out-of-range slot is reported */
-    const int bad = or_pool_step(&desc, pool, slots, B, q, k, v, beta, g, o, threads);
+    const int bad = or_pool_step(&desc, pool, slots, B, q, k, v, beta, g, o, threads, (t & 1) ? om : NULL);
     if (bad != (t == 3 ? 1 : 0)) return -2;
     ++steps;
   }
@@ -84,7 +85,7 @@ static int run_pool(int unit, int gate, int scale_mode, int fit, int scale_bits,
   (void)or_bf16_up(3.3f);
   (void)or_bf16_nearest(3.3f);
   free(blk); free(Spre); free(e);
-  free(q); free(k); free(v); free(beta); free(g); free(o);
+  free(q); free(k); free(v); free(beta); free(g); free(o); free(om);
   free(S); free(pool); free(kinds); free(omega);
   return steps;
 }

@@ -7,7 +7,8 @@ Bar (applied per decode step):
     An excused head is re-synchronised by writing the oracle's bytes into the
     device pool (data flows oracle -> device only);
   * readout o: relative L2 error <= 1e-4 against the oracle (per step, over
-    all requests and heads) and per head <= 1e-3.
+    all requests and heads) and per head <= 1e-3 of ||o|| + 0.02 ||m||, with
+    m the readout magnitude sum_i |q_i| |S_ij| (compare_o).
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ TIE_WINDOW = 1e-6
 MAX_EXCUSED_FRACTION = 1e-4
 O_REL_L2 = 1e-4
 O_WORST_HEAD = 1e-3
+MAG_WEIGHT = 0.02
 
 
 @dataclasses.dataclass
@@ -40,11 +42,20 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a - b))
 
 
-def compare_o(o_dev, o_ref, rep: StepReport):
+def compare_o(o_dev, o_ref, rep: StepReport, o_mag=None):
+    """Readout bar.  Over the whole step: relative L2.  Per head: the error
+    relative to ||o|| + MAG_WEIGHT ||m||, where m_j = sum_i |q_i| |S_ij| (the
+    oracle's readout magnitude).  Both sides are sums of 128 products in
+    different orders, so a head whose readout cancels (|o_j| << m_j) carries
+    a rounding difference of order 2^-24 * 64 * m_j that ||o|| alone would
+    not account for (|fl(x.y) - x.y| <= gamma_n |x|.|y|); with the weight
+    below the per-head bound allows 2e-5 ||m|| on top of 1e-3 ||o||."""
     rep.o_rel_l2 = rel_l2(o_dev, o_ref)
     od = np.asarray(o_dev, np.float64).reshape(-1, D)
     orf = np.asarray(o_ref, np.float64).reshape(-1, D)
     den = np.linalg.norm(orf, axis=1)
+    if o_mag is not None:
+        den = den + MAG_WEIGHT * np.linalg.norm(np.asarray(o_mag, np.float64).reshape(-1, D), axis=1)
     num = np.linalg.norm(od - orf, axis=1)
     per = np.where(den > 0, num / np.maximum(den, 1e-300), num)
     rep.o_worst_head = float(per.max()) if per.size else 0.0

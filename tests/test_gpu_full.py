@@ -166,7 +166,7 @@ def test_config4_every_head_of_eight_requests(torch_dev, orc):
     torch.cuda.synchronize()
     assert bad == 0 and pool.qdr_poll_device_error() == 0
     rep = parity.StepReport()
-    parity.compare_o(o.cpu().numpy()[req], o_ref, rep)
+    parity.compare_o(o.cpu().numpy()[req], o_ref, rep, ref.last_o_mag)
     parity.compare_pool(orc, ref, view, rslots, parity.step_state_fn(orc, ref, prev, rslots, sub), rep)
     parity.assert_step_ok(rep, "config 4 decode step")
     print(f"config 4: every head of {n} requests matches after the step: o rel L2 {rep.o_rel_l2:.2e}, "
@@ -199,7 +199,7 @@ def test_config5_every_head_of_a_request(torch_dev, orc, request_index):
         o_ref, bad = ref.step(rs, *sub, threads=16)
         assert bad == 0
         rep = parity.StepReport()
-        parity.compare_o(o[r:r + 1].cpu().numpy(), o_ref, rep)
+        parity.compare_o(o[r:r + 1].cpu().numpy(), o_ref, rep, ref.last_o_mag)
         parity.compare_pool(orc, ref, view, rs, parity.step_state_fn(orc, ref, prev, rs, sub), rep)
         parity.assert_step_ok(rep, f"config 5 request {r} step {s}")
         worst, worst_head = max(worst, rep.o_rel_l2), max(worst_head, rep.o_worst_head)

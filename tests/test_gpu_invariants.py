@@ -107,7 +107,7 @@ class Case:
         o_ref, bad = self.ref.step(self.slots, *ins, threads=8)
         o_dev = o.cpu().numpy()
         rep = parity.StepReport()
-        parity.compare_o(o_dev, o_ref, rep)
+        parity.compare_o(o_dev, o_ref, rep, self.ref.last_o_mag)
         parity.compare_pool(self.orc, self.ref, self.dev, self.slots,
                             parity.step_state_fn(self.orc, self.ref, prev, self.slots, ins), rep)
         parity.assert_step_ok(rep, what)

@@ -143,7 +143,7 @@ def run_step_pair(torch, orc, dev, ref, slots, inputs, threads=8):
     o_ref, bad = ref.step(slots, *inputs, threads=threads)
     o_dev = o.cpu().numpy()
     rep = parity.StepReport()
-    parity.compare_o(o_dev, o_ref, rep)
+    parity.compare_o(o_dev, o_ref, rep, ref.last_o_mag)
     parity.compare_pool(orc, ref, dev, slots, parity.step_state_fn(orc, ref, prev, slots, inputs), rep)
     return rep, o_dev, o_ref, bad
 
@@ -265,7 +265,7 @@ def trajectory(torch, orc, cid, steps, threads=16, sb=32, requests=None):
         sub = tuple(np.ascontiguousarray(x[req]) for x in inputs)
         o_ref, bad = ref.step(rslots, *sub, threads=threads)
         rep = parity.StepReport()
-        parity.compare_o(o.cpu().numpy()[req], o_ref, rep)
+        parity.compare_o(o.cpu().numpy()[req], o_ref, rep, ref.last_o_mag)
         parity.compare_pool(orc, ref, dev, rslots, parity.step_state_fn(orc, ref, prev, rslots, sub), rep)
         parity.assert_step_ok(rep, f"config {cid} sb={sb} step {s}")
         assert bad == 0

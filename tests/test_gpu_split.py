@@ -36,7 +36,7 @@ def split_step_pair(torch, orc, dev, ref, slots, inputs, sr, sw, threads=8):
     o_ref, bad = ref.step(slots, *inputs, threads=threads)
     torch.cuda.synchronize()
     rep = parity.StepReport()
-    parity.compare_o(o_dev, o_ref, rep)
+    parity.compare_o(o_dev, o_ref, rep, ref.last_o_mag)
     parity.compare_pool(orc, ref, dev, slots, parity.step_state_fn(orc, ref, prev, slots, inputs), rep)
     return rep, o_dev, bad
 

@@ -413,3 +413,34 @@ def test_error_recursion(orc):
         # the readout used the state before requantisation
         assert np.linalg.norm(o - S_pre.astype(np.float64).T @ q) <= 1e-6 * np.linalg.norm(o)
         X_prev = X
+
+
+def test_readout_magnitude(orc):
+    """m_j = sum_i |q_i| |S_ij| (the error scale the readout checks use):
+    float64 closed form within one fp32 rounding; the pool step reports it for
+    the updated state of every head, zero for padding rows."""
+    g = RNG(90)
+    S = synth.random_state(90, 1, 1)[0, 0]
+    q = f32(g.standard_normal(D))
+    m = orc.readout_magnitude(S, q)
+    ref = np.abs(q.astype(np.float64)) @ np.abs(S.astype(np.float64))
+    assert np.all(np.abs(m - ref) <= 2.0 ** -23 * ref)
+    assert np.all(m >= np.abs(orc.readout(S, q)))
+    kinds = np.array([8, 6, 32], np.uint8)
+    P = orc.Pool(2, 3, kinds, np.ones((3, D), np.float32)).alloc()
+    P.pack(np.arange(2), synth.random_state(91, 2, 3))
+    before = P.mem.copy()
+    qq = f32(g.standard_normal((2, 3, D)))
+    kk = f32(unit(g.standard_normal((2, 3, D))))
+    vv = f32(g.standard_normal((2, 3, D)))
+    bb = f32(g.uniform(0, 1, (2, 3)))
+    aa = f32(g.uniform(0.5, 1, (2, 3)))
+    o, bad = P.step(np.array([1, -1], np.int32), qq, kk, vv, bb, aa)
+    assert bad == 0 and np.all(P.last_o_mag[1] == 0)
+    for h in range(3):
+        hk = P.head_kinds(h)
+        off = P.slot_stride + int(P.head_off[h])
+        e, r, c = orc.decode_block(hk, 0, 0, before[off:off + P.block_size(h)])
+        _, _, _, o_h, S_pre = orc.head_step(hk, e, r, c, np.ones(D), qq[0, h], kk[0, h], vv[0, h],
+                                            float(bb[0, h]), np.full(D, aa[0, h], np.float32))
+        assert np.array_equal(P.last_o_mag[0, h], orc.readout_magnitude(S_pre, qq[0, h]))

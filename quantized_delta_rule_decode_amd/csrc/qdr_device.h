@@ -185,9 +185,16 @@ __device__ __forceinline__ uint4 load_granule(rsrc_t rs, uint32_t voff, uint32_t
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// A 16-byte store may read its data registers after the next instructions
+// have issued.  The compiler keeps those registers untouched for the
+// required wait state only when the store has no scalar offset register (it
+// takes a store with an SGPR soffset to have read its data already); on this
+// GPU that does not hold -- an overwrite right behind such a store reached
+// memory for some lanes -- so the whole offset goes into the lane offset and
+// soffset is the constant 0.
 __device__ __forceinline__ void store_granule(rsrc_t rs, uint4 t, uint32_t voff, uint32_t soff) {
   __attribute__((ext_vector_type(4))) unsigned int v = {t.x, t.y, t.z, t.w};
-  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, 2);   // nontemporal: written once per step
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff + soff, 0, 2);   // nontemporal: written once per step
 }
 
 __device__ __forceinline__ float load_f32(rsrc_t rs, uint32_t voff, uint32_t soff) {
@@ -255,6 +262,26 @@ __device__ __forceinline__ void store_column(rsrc_t rs, const uint32_t *ow, uint
 
 __device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
+// The lane index (0..63), computed afresh with v_mbcnt where it is used: the
+// byte offsets of the final stores would otherwise stay live in registers
+// from the item's loads to its stores, across the whole tile.
+__device__ __forceinline__ uint32_t lane_now() {
+  uint32_t r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+  return r;
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// The fp32 tile of one wave: lane l holds columns l and l + 64 of the wave's
+// 64 rows; four consecutive rows of a column share one 4-register vector
+// (v[c][g][e] = row 4g + e, column l + 64c).
+struct Tile {
+  v4f v[2][16];
+  __device__ __forceinline__ float get(int c, int ii) const { return v[c][ii >> 2][ii & 3]; }
+  __device__ __forceinline__ void set(int c, int ii, float x) { v[c][ii >> 2][ii & 3] = x; }
+};
+
 // Row reduction of |S| over the 128 columns of each of this wave's 64 rows.
 // SUM: the fold-by-halves tree over the 128 columns (pairs j/j+64 are the
 // lane's own two columns; then j/j+32 by
@@ -262,7 +289,7 @@ __device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cas
 // transpose).  MAX: the same tree with max.  Returns the value of row
 // 64w + lane.  red: this wave's [64][20] LDS scratch.
 template <bool MAX>
-__device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red)[20], int lane) {
+__device__ __forceinline__ float row_reduce(const Tile &S, float (*red)[20], int lane) {
   // rows are taken four at a time so that only a handful of partials are
   // live next to the tile: rows 4s..4s+3 -> two permlane32 partials -> one
   // permlane16 partial holding row 4s + {0,2,1,3}[lane/16] for column
@@ -275,8 +302,8 @@ __device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int r0 = 4 * s + 2 * t, r1 = r0 + 1;
-      const float p0 = MAX ? fmaxf(fabsf(S[0][r0]), fabsf(S[1][r0])) : fabsf(S[0][r0]) + fabsf(S[1][r0]);
-      const float p1 = MAX ? fmaxf(fabsf(S[0][r1]), fabsf(S[1][r1])) : fabsf(S[0][r1]) + fabsf(S[1][r1]);
+      const float p0 = MAX ? fmaxf(fabsf(S.get(0, r0)), fabsf(S.get(1, r0))) : fabsf(S.get(0, r0)) + fabsf(S.get(1, r0));
+      const float p1 = MAX ? fmaxf(fabsf(S.get(0, r1)), fabsf(S.get(1, r1))) : fabsf(S.get(0, r1)) + fabsf(S.get(1, r1));
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
       const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
       h1[t] = MAX ? fmaxf(x, y) : x + y;
@@ -314,7 +341,7 @@ __device__ __forceinline__ float row_reduce(const float (&S)[2][64], float (*red
 // OFF4 (INT4 only): the codes are converted as z/16 and gsh holds 16 g_i, so
 // z' * (16 g) is the same real number as z * g and rounds identically.
 template <int BITS, bool CHAIN, bool OFF4 = false>
-__device__ __forceinline__ void restore_rows(float (&S)[2][64], float (&acc)[2],
+__device__ __forceinline__ void restore_rows(Tile &S, float (&acc)[2],
                                              const uint32_t (&wd)[2][Kind<BITS>::NW],
                                              const float (&colc)[2], const float *gsh,
                                              const float *xsh, int row0) {
@@ -339,7 +366,7 @@ __device__ __forceinline__ void restore_rows(float (&S)[2][64], float (&acc)[2],
         } else {
           sp = gg[e] * __uint_as_float(field_bits<32>(wd[c], ii));
         }
-        S[c][ii] = sp;
+        S.set(c, ii, sp);
         if (CHAIN) acc[c] = __builtin_fmaf(xx[e], sp, acc[c]);
       }
     }
@@ -348,15 +375,31 @@ __device__ __forceinline__ void restore_rows(float (&S)[2][64], float (&acc)[2],
 }
 
 // acc_c = fma(x_i, S_ic, acc_c) over this wave's 64 rows, in order.
-__device__ __forceinline__ void chain_rows(const float (&S)[2][64], float (&acc)[2], const float *xsh, int row0) {
+__device__ __forceinline__ void chain_rows(const Tile &S, float (&acc)[2], const float *xsh, int row0) {
 #pragma unroll
   for (int i4 = 0; i4 < 16; ++i4) {
     const float4 x4 = lds4(&xsh[row0 + 4 * i4]);
     const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[0] = __builtin_fmaf(xx[e], S[0][4 * i4 + e], acc[0]);
-      acc[1] = __builtin_fmaf(xx[e], S[1][4 * i4 + e], acc[1]);
+      acc[0] = __builtin_fmaf(xx[e], S.get(0, 4 * i4 + e), acc[0]);
+      acc[1] = __builtin_fmaf(xx[e], S.get(1, 4 * i4 + e), acc[1]);
+    }
+    QDR_FENCE();
+  }
+}
+
+// The rank-1 delta update of this wave's tile: S_ij = fma(b_i, delta_j, S_ij).
+// bsh: the wave's b table (b_i of rows row0 ..).
+__device__ __forceinline__ void delta_update(Tile &S, const float (&dl)[2], const float *bsh) {
+#pragma unroll
+  for (int i4 = 0; i4 < 16; ++i4) {
+    const float4 b4 = lds4(bsh + 4 * i4);
+    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      S.set(0, 4 * i4 + e, __builtin_fmaf(bb[e], dl[0], S.get(0, 4 * i4 + e)));
+      S.set(1, 4 * i4 + e, __builtin_fmaf(bb[e], dl[1], S.get(1, 4 * i4 + e)));
     }
     QDR_FENCE();
   }
@@ -381,14 +424,13 @@ __device__ __forceinline__ void row_groups(const float *t, F &&f) {
 
 // chain_rows with its table reads issued A groups ahead (row_groups)
 template <int A>
-__device__ __forceinline__ void chain_rows_ahead(const float (&S)[2][64], float (&acc)[2], const float *xsh,
-                                                 int row0) {
+__device__ __forceinline__ void chain_rows_ahead(const Tile &S, float (&acc)[2], const float *xsh, int row0) {
   row_groups<A>(xsh + row0, [&](int i4, const float4 x4) {
     const float xx[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[0] = __builtin_fmaf(xx[e], S[0][4 * i4 + e], acc[0]);
-      acc[1] = __builtin_fmaf(xx[e], S[1][4 * i4 + e], acc[1]);
+      acc[0] = __builtin_fmaf(xx[e], S.get(0, 4 * i4 + e), acc[0]);
+      acc[1] = __builtin_fmaf(xx[e], S.get(1, 4 * i4 + e), acc[1]);
     }
   });
 }
@@ -503,10 +545,10 @@ struct Occupancy {
 };
 
 // The work of one (request b, head h) of kind BITS; sh is the workgroup's
-// LDS block.
+// LDS block; w the wave of this lane (0 or 1, uniform).
 template <int BITS, int MODE, int GATE, int SCALE, int FIT>
 __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const int b, const int h,
-                                          const uint64_t head_off, const uint32_t code_bytes) {
+                                          const uint64_t head_off, const uint32_t code_bytes, const int w) {
   using K = Kind<BITS>;
   constexpr bool INT = K::is_int;
   constexpr float QMAX = (float)K::qmax_i;
@@ -518,15 +560,13 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   constexpr uint32_t SCB = SC16 ? 2u : 4u;   // bytes per stored factor
   constexpr float GSCALE = OFF4 ? 16.0f : 1.0f;
 
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63;
+  const int l = threadIdx.x & 63;
   const int row = 64 * w + l;
   const size_t bh = (size_t)b * P.H + h;
   const int slot = P.slots[b];
 
   if (slot < 0 || slot >= P.num_slots) {
-    if (slot != -1 && tid == 0) atomicOr(P.err, 1u);
+    if (slot != -1 && row == 0) atomicOr(P.err, 1u);
     if (writes_o(MODE) && w == 0 && P.o != nullptr) {
       out_o<io16(MODE)>(P, bh * kDim + l, 0.0f);     // wave 0 and 1 cover columns 0..127
       out_o<io16(MODE)>(P, bh * kDim + 64 + l, 0.0f);
@@ -544,7 +584,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
   const uint32_t r_off = code_bytes;                              // r[128]
   const uint32_t c_off = code_bytes + kDim * SCB;                 // c[128]
 
-  float S[2][64];
+  Tile S;
   float colc[2] = {1.0f, 1.0f};
 
   // ---------------- load codes (both columns of this lane, this wave's rows)
@@ -583,10 +623,25 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
 
   // ---------------- per-row scalars of this lane's row, broadcast via LDS
   if (restores(MODE)) sh.g[row] = INT ? (a_row * rn_div(r_raw, QMAX)) * GSCALE : a_row;
+  const float b_row = beta_b * kr;
   if (has_readout(MODE)) {
     sh.k[row] = kr;
-    sh.b[row] = beta_b * kr;
+    sh.b[row] = b_row;
     sh.q[row] = qr;
+    if (w == 1) {
+      // v waits in the delta slots (wave 1 forms delta there)
+      sh.d[l] = vcol[0];
+      sh.d[l + 64] = vcol[1];
+    }
+  }
+  // omega waits in the row's 1/r slot (overwritten by 1/r), so neither it
+  // nor v holds a register across the restore and the update
+  if (INT && dual(SCALE)) sh.ir[row] = omega_row;
+  if (has_readout(MODE)) {
+    // each wave's part of q . beta k (order free: readout only), now, so
+    // that q and beta k hold no registers across the restore
+    const float qb_part = wave_sum(qr * b_row);
+    if (l == 0) sh.qb[w] = qb_part;
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -605,8 +660,8 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     float *dst = P.S_out + bh * kDim * kDim;
 #pragma unroll
     for (int ii = 0; ii < 64; ++ii) {
-      dst[(64 * w + ii) * kDim + l] = S[0][ii];
-      dst[(64 * w + ii) * kDim + 64 + l] = S[1][ii];
+      dst[(64 * w + ii) * kDim + l] = S.get(0, ii);
+      dst[(64 * w + ii) * kDim + 64 + l] = S.get(1, ii);
     }
     return;
   }
@@ -615,72 +670,52 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     const float *src = P.S_in + bh * kDim * kDim;
 #pragma unroll
     for (int ii = 0; ii < 64; ++ii) {
-      S[0][ii] = src[(64 * w + ii) * kDim + l];
-      S[1][ii] = src[(64 * w + ii) * kDim + 64 + l];
+      S.set(0, ii, src[(64 * w + ii) * kDim + l]);
+      S.set(1, ii, src[(64 * w + ii) * kDim + 64 + l]);
     }
   }
   if (MODE == MODE_RESET) {
 #pragma unroll
-    for (int ii = 0; ii < 64; ++ii) { S[0][ii] = 0.0f; S[1][ii] = 0.0f; }
+    for (int ii = 0; ii < 64; ++ii) { S.set(0, ii, 0.0f); S.set(1, ii, 0.0f); }
   }
 
-  // ---------------- delta update
-  float oq[2] = {0.0f, 0.0f};
-  float dl[2] = {0.0f, 0.0f};
+  // ---------------- delta update, and the readout as soon as delta is known
+  // (tolerance-checked, any summation order):
+  //   o = S_t^T q = S'^T q + (q . b) delta,
+  // wave 1's part of S'^T q handed to wave 0 with delta
   if (has_readout(MODE)) {
     if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
-    const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
-    if (l == 0) sh.qb[w] = qb_part;
     __syncthreads();
     float acc2[2] = {0.0f, 0.0f};
     if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
     chain_rows(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
     if (w == 1) {
-      sh.d[l] = vcol[0] - acc2[0];
-      sh.d[l + 64] = vcol[1] - acc2[1];
-      oq[0] = acc1[0]; oq[1] = acc1[1];
-    } else {
-      oq[0] = acc2[0]; oq[1] = acc2[1];
+      sh.d[l] = sh.d[l] - acc2[0];
+      sh.d[l + 64] = sh.d[l + 64] - acc2[1];
+      sh.x[l] = acc1[0];          // wave 1's readout part; wave 0's u part has been read
+      sh.x[l + 64] = acc1[1];
     }
     __syncthreads();
-    dl[0] = sh.d[l];
-    dl[1] = sh.d[l + 64];
-    if constexpr (MODE == MODE_READOUT) {
-      // readout-first launch: o = S'^T q + (q . b) delta as in the step;
-      // the state is neither updated nor stored (the write-back launch does it)
-      if (w == 1) { sh.x[l] = oq[0]; sh.x[l + 64] = oq[1]; }
-      __syncthreads();
-      if (w == 0 && P.o != nullptr) {
-        const float qb_all = sh.qb[0] + sh.qb[1];
-        out_o<io16(MODE)>(P, bh * kDim + l, (oq[0] + sh.x[l]) + qb_all * dl[0]);
-        out_o<io16(MODE)>(P, bh * kDim + 64 + l, (oq[1] + sh.x[l + 64]) + qb_all * dl[1]);
-      }
-      return;
+    float dl[2] = {sh.d[l], sh.d[l + 64]};
+    if (writes_o(MODE) && w == 0 && P.o != nullptr) {
+      const float qb_all = sh.qb[0] + sh.qb[1];
+      out_o<io16(MODE)>(P, bh * kDim + l, (acc2[0] + sh.x[l]) + qb_all * dl[0]);
+      out_o<io16(MODE)>(P, bh * kDim + 64 + l, (acc2[1] + sh.x[l + 64]) + qb_all * dl[1]);
     }
-#pragma unroll
-    for (int i4 = 0; i4 < 16; ++i4) {
-      const float4 b4 = lds4(&sh.b[64 * w + 4 * i4]);
-      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ii = 4 * i4 + e;
-        S[0][ii] = __builtin_fmaf(bb[e], dl[0], S[0][ii]);
-        S[1][ii] = __builtin_fmaf(bb[e], dl[1], S[1][ii]);
-      }
-      QDR_FENCE();
-    }
+    // readout-first launch: the state is neither updated nor stored (the
+    // write-back launch does it)
+    if constexpr (MODE == MODE_READOUT) return;
+    delta_update(S, dl, &sh.b[64 * w]);
   }
-  // readout (tolerance-checked, any summation order):
-  //   o = S_t^T q = S'^T q + (q . b) delta
-  float ocol[2] = {oq[0], oq[1]};
 
   // ---------------- requantise
   if (INT) {
     // row factor
     float r_row, m_row = 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
     if (dual(SCALE)) {
       m_row = row_reduce<false>(S, sh.red[w], l) * 0.0078125f;
-      const float nu = rn_div(m_row, omega_row);
+      const float nu = rn_div(m_row, sh.ir[row]);   // omega of the row
       r_row = (nu == 0.0f) ? 1.0f : rn_sqrt(nu);
     } else {
       const float mx = row_reduce<true>(S, sh.red[w], l);
@@ -689,7 +724,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     if constexpr (SC16) r_row = bf16_up(r_row);
     sh.ir[row] = rn_div(1.0f, r_row);
     if (FIT) sh.m[row] = m_row;
-    store_sc<SC16>(rs, r_row, (uint32_t)l, r_off + (uint32_t)w * 64u * SCB);
+    store_sc<SC16>(rs, r_row, lane_now(), r_off + (uint32_t)w * 64u * SCB);
     __builtin_amdgcn_wave_barrier();
 
     // Y = S / r (in place) and the column maximum
@@ -705,8 +740,8 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const float y = S[c][4 * i4 + e] * rr[e];
-          S[c][4 * i4 + e] = y;
+          const float y = S.get(c, 4 * i4 + e) * rr[e];
+          S.set(c, 4 * i4 + e, y);
           cm[c][e >> 1] = fmaxf(cm[c][e >> 1], fabsf(y));
         }
       }
@@ -717,7 +752,6 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
       sh.cmax[w][l] = fmaxf(cm[0][0], cm[0][1]);
       sh.cmax[w][l + 64] = fmaxf(cm[1][0], cm[1][1]);
     }
-    if (is_step(MODE) && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
     __syncthreads();
     if (dual(SCALE)) {
 #pragma unroll
@@ -736,7 +770,7 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     constexpr float INVQ = INT ? 1.0f / (QMAX > 0.0f ? QMAX : 1.0f) : 0.0f;
     {
       uint32_t ow[2][K::NW];
-      uint32_t acc[2] = {0u, 0u};
+      uint32_t pacc[2] = {0u, 0u};
 #pragma unroll
       for (int i4 = 0; i4 < 16; ++i4) {
         float mm[4] = {0, 0, 0, 0};
@@ -750,13 +784,13 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
           const int ii = 4 * i4 + e;
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const float t = __builtin_fmaf(S[c][ii], wq[c], kMagic);
+            const float t = __builtin_fmaf(S.get(c, ii), wq[c], kMagic);
             tb[c][e] = __float_as_uint(t);
-            if (BITS != 8) put_field<BITS>(ow[c], acc[c], __float_as_uint(t), ii);
+            if (BITS != 8) put_field<BITS>(ow[c], pacc[c], __float_as_uint(t), ii);
             if (FIT) {
               const float zeta = (t - kMagic) * INVQ;
               const float pz = mm[e] * zeta;
-              nacc[c] = __builtin_fmaf(pz, S[c][ii], nacc[c]);
+              nacc[c] = __builtin_fmaf(pz, S.get(c, ii), nacc[c]);
               dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
             }
           }
@@ -773,15 +807,17 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
         }
         QDR_FENCE();
       }
+      const uint32_t ln = lane_now();
 #pragma unroll
-      for (int c = 0; c < 2; ++c) store_column<BITS>(rs, ow[c], (uint32_t)(l + 64 * c) * 16u, half_off);
+      for (int c = 0; c < 2; ++c) store_column<BITS>(rs, ow[c], (ln + 64u * c) * 16u, half_off);
     }
     // column factor
     if (dual(SCALE)) {
       if (!FIT) {
         if (w == 0) {
-          store_sc<SC16>(rs, c0[0], (uint32_t)l, c_off);
-          store_sc<SC16>(rs, c0[1], (uint32_t)l + 64u, c_off);
+          const uint32_t ln = lane_now();
+          store_sc<SC16>(rs, c0[0], ln, c_off);
+          store_sc<SC16>(rs, c0[1], ln + 64u, c_off);
         }
       } else {
         if (w == 0) {
@@ -799,10 +835,10 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
               const float mm[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float t = __builtin_fmaf(S[c][4 * i4 + e], wq[c], kMagic);
+                const float t = __builtin_fmaf(S.get(c, 4 * i4 + e), wq[c], kMagic);
                 const float zeta = (t - kMagic) * INVQ;
                 const float pz = mm[e] * zeta;
-                nn = __builtin_fmaf(pz, S[c][4 * i4 + e], nn);
+                nn = __builtin_fmaf(pz, S.get(c, 4 * i4 + e), nn);
                 dd = __builtin_fmaf(pz, zeta, dd);
               }
             }
@@ -815,28 +851,19 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     }
   } else {
     // FP16 / FP32 rows: store the updated values themselves
-    if (is_step(MODE) && w == 1) { sh.x[l] = ocol[0]; sh.x[l + 64] = ocol[1]; }
-    __syncthreads();
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       uint32_t ow[K::NW];
-      uint32_t acc = 0;
+      uint32_t pacc = 0;
 #pragma unroll
       for (int ii = 0; ii < 64; ++ii) {
         uint32_t f;
-        if (BITS == 16) f = (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])));
-        else f = __float_as_uint(S[c][ii]);
-        put_field<BITS>(ow, acc, f, ii);
+        if (BITS == 16) f = (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S.get(c, ii))));
+        else f = __float_as_uint(S.get(c, ii));
+        put_field<BITS>(ow, pacc, f, ii);
       }
-      store_column<BITS>(rs, ow, (uint32_t)(l + 64 * c) * 16u, half_off);
+      store_column<BITS>(rs, ow, (lane_now() + 64u * c) * 16u, half_off);
     }
-  }
-
-  // ---------------- the readout
-  if (writes_o(MODE) && w == 0 && P.o != nullptr) {
-    const float qb_all = sh.qb[0] + sh.qb[1];
-    out_o<io16(MODE)>(P, bh * kDim + l, (ocol[0] + sh.x[l]) + qb_all * dl[0]);
-    out_o<io16(MODE)>(P, bh * kDim + 64 + l, (ocol[1] + sh.x[l + 64]) + qb_all * dl[1]);
   }
 }
 
@@ -855,7 +882,8 @@ k_head(const LaunchArgs P) {
   const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(e.info.off >> 32)) << 32) |
                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)e.info.off);
   const uint32_t code_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)e.info.code_bytes);
-  head_body<BITS, MODE, GATE, SCALE, FIT>(P, sh, b, e.h, off, code_bytes);
+  head_body<BITS, MODE, GATE, SCALE, FIT>(P, sh, b, e.h, off, code_bytes,
+                                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
 }
 
 // Every integer kind in one launch.  head_list interleaves the integer heads
@@ -882,10 +910,11 @@ k_head_int(const LaunchArgs P) {
   const uint32_t code_bytes = wv[2];
   const int kind = (int)((wv[3] >> 16) & 0xFFu);
   const int h = (int)wv[4];
-  if (kind == 6) head_body<6, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
-  else if (kind == 8) head_body<8, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
-  else if (kind == 4) head_body<4, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
-  else head_body<2, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (kind == 6) head_body<6, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes, w);
+  else if (kind == 8) head_body<8, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes, w);
+  else if (kind == 4) head_body<4, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes, w);
+  else head_body<2, MODE, GATE, SCALE, FIT>(P, sh, b, h, off, code_bytes, w);
 }
 
 // Row i's program word, broadcast from lane i of the per-lane table register
@@ -1062,9 +1091,10 @@ k_rows(const LaunchArgs P) {
   sh.qm[row] = my_q;
   if (FIT) sh.iq[row] = my_int ? rn_div(1.0f, my_q) : 0.0f;
   if (restores(MODE)) sh.g[row] = my_int ? a_row * rn_div(r_raw, my_q) : a_row;
+  const float b_row = beta_b * kr;
   if (has_readout(MODE)) {
     sh.k[row] = kr;
-    sh.b[row] = beta_b * kr;
+    sh.b[row] = b_row;
     sh.q[row] = qr;
     // v waits in the delta slots (wave 1 forms delta there) and omega in the
     // 1/r slot (overwritten by 1/r), so neither holds a register meanwhile
@@ -1075,7 +1105,7 @@ k_rows(const LaunchArgs P) {
   // ---------------- stage the code words in LDS: the first eight chunks
   // from registers, any further ones (halves over 8 KiB) in batches of eight
   // loads ahead of their writes
-  float S[2][64];
+  Tile S;
   if (restores(MODE)) {
 #pragma unroll
     for (uint32_t u = 0; u < 8u; ++u)
@@ -1124,7 +1154,7 @@ k_rows(const LaunchArgs P) {
       for (int c = 0; c < 2; ++c) {
         // FP32 rows have width 0 here (and give 0); R2 redoes them
         const int32_t z = sext_low(__builtin_amdgcn_alignbit(wq[ii][2 + c], wq[ii][c], pe), rp_width(pe));
-        S[c][ii] = ((float)z * gi) * colc[c];
+        S.set(c, ii, ((float)z * gi) * colc[c]);
       }
       if (ii + kAhead < 64) fetch(ii + kAhead);
       __builtin_amdgcn_sched_barrier(0);
@@ -1146,8 +1176,8 @@ k_rows(const LaunchArgs P) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const uint32_t f = __builtin_amdgcn_alignbit(wp[kDim + 64 * c], wp[64 * c], pe);
-            S[c][ii] = gi * (f32row ? __uint_as_float(f)
-                                    : __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu))));
+            S.set(c, ii, gi * (f32row ? __uint_as_float(f)
+                                      : __half2float(__ushort_as_half((unsigned short)(f & 0xFFFFu)))));
           }
         }
       }
@@ -1159,8 +1189,8 @@ k_rows(const LaunchArgs P) {
     float *dst = P.S_out + bh * kDim * kDim;
 #pragma unroll
     for (int ii = 0; ii < 64; ++ii) {
-      dst[(64 * w + ii) * kDim + l] = S[0][ii];
-      dst[(64 * w + ii) * kDim + 64 + l] = S[1][ii];
+      dst[(64 * w + ii) * kDim + l] = S.get(0, ii);
+      dst[(64 * w + ii) * kDim + 64 + l] = S.get(1, ii);
     }
     return;
   }
@@ -1168,13 +1198,13 @@ k_rows(const LaunchArgs P) {
     const float *src = P.S_in + bh * kDim * kDim;
 #pragma unroll
     for (int ii = 0; ii < 64; ++ii) {
-      S[0][ii] = src[(64 * w + ii) * kDim + l];
-      S[1][ii] = src[(64 * w + ii) * kDim + 64 + l];
+      S.set(0, ii, src[(64 * w + ii) * kDim + l]);
+      S.set(1, ii, src[(64 * w + ii) * kDim + 64 + l]);
     }
   }
   if (MODE == MODE_RESET) {
 #pragma unroll
-    for (int ii = 0; ii < 64; ++ii) { S[0][ii] = 0.0f; S[1][ii] = 0.0f; }
+    for (int ii = 0; ii < 64; ++ii) { S.set(0, ii, 0.0f); S.set(1, ii, 0.0f); }
   }
 
   // ---------------- delta update (same hand-off as k_head)
@@ -1182,7 +1212,7 @@ k_rows(const LaunchArgs P) {
   float dl[2] = {0.0f, 0.0f};
   if (has_readout(MODE)) {
     if (w == 0) { sh.x[l] = acc1[0]; sh.x[l + 64] = acc1[1]; }
-    const float qb_part = wave_sum(sh.q[row] * sh.b[row]);
+    const float qb_part = wave_sum(qr * b_row);
     if (l == 0) sh.qb[w] = qb_part;
     __syncthreads();
     float acc2[2] = {0.0f, 0.0f};
@@ -1215,8 +1245,8 @@ k_rows(const LaunchArgs P) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 4 * i4 + e;
-        S[0][ii] = __builtin_fmaf(bb[e], dl[0], S[0][ii]);
-        S[1][ii] = __builtin_fmaf(bb[e], dl[1], S[1][ii]);
+        S.set(0, ii, __builtin_fmaf(bb[e], dl[0], S.get(0, ii)));
+        S.set(1, ii, __builtin_fmaf(bb[e], dl[1], S.get(1, ii)));
       }
     });
   }
@@ -1254,8 +1284,8 @@ k_rows(const LaunchArgs P) {
         const int rank = __builtin_popcountll(pivots & ((1ull << ii) - 1ull));
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          stash[rank * 128 + l + 64 * c] = f32row ? __float_as_uint(S[c][ii])
-                                                  : (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S[c][ii])));
+          stash[rank * 128 + l + 64 * c] = f32row ? __float_as_uint(S.get(c, ii))
+                                                  : (uint32_t)__half_as_ushort(__float2half_rn(pin_f32(S.get(c, ii))));
       }
     }
   }
@@ -1276,8 +1306,8 @@ k_rows(const LaunchArgs P) {
       const int ii = 4 * i4 + e;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const float y = S[c][ii] * rr[e];
-        S[c][ii] = y;
+        const float y = S.get(c, ii) * rr[e];
+        S.set(c, ii, y);
         cm[c] = fmaxf(cm[c], fabsf(y));
       }
     }
@@ -1316,7 +1346,7 @@ k_rows(const LaunchArgs P) {
     nacc[0] = sh.d[l]; nacc[1] = sh.d[l + 64];
     dacc[0] = sh.y[l]; dacc[1] = sh.y[l + 64];
   }
-  uint32_t (&T)[2][64] = reinterpret_cast<uint32_t (&)[2][64]>(S);   // code bits, in place
+  // code bits replace the values in place (the tile holds the bit patterns)
   row_groups<kAhead>(&sh.qm[64 * w], [&](int i4, const float4 q4) {
     const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
     float4 m4 = {0, 0, 0, 0}, iq4 = {0, 0, 0, 0};
@@ -1328,7 +1358,7 @@ k_rows(const LaunchArgs P) {
       const int ii = 4 * i4 + e;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const float y = S[c][ii];
+        const float y = S.get(c, ii);
         const float t = __builtin_fmaf(y, ec[c] * qq[e], kMagic);
         if (FIT) {
           // pivot rows: 1/q is stored as 0, so they add exact zeros
@@ -1337,7 +1367,7 @@ k_rows(const LaunchArgs P) {
           nacc[c] = __builtin_fmaf(pz, y, nacc[c]);
           dacc[c] = __builtin_fmaf(pz, zeta, dacc[c]);
         }
-        T[c][ii] = __float_as_uint(t);
+        S.set(c, ii, t);
       }
     }
   });
@@ -1356,8 +1386,8 @@ k_rows(const LaunchArgs P) {
         const int ii = 8 * g8 + e;
         if (!((pivots >> ii) & 1u)) continue;
         const int rank = __builtin_popcountll(pivots & ((1ull << ii) - 1ull));
-        T[0][ii] = stash[rank * 128 + l];
-        T[1][ii] = stash[rank * 128 + l + 64];
+        S.set(0, ii, __uint_as_float(stash[rank * 128 + l]));
+        S.set(1, ii, __uint_as_float(stash[rank * 128 + l + 64]));
       }
     }
   }
@@ -1389,10 +1419,11 @@ k_rows(const LaunchArgs P) {
           const int ii = 8 * b8 + e;
           const uint32_t pe = pb[b8 & 1][e];
           uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
-          o[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_pack_shift(pe));
-          o[64] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_pack_shift(pe));
-          win[0] = __builtin_amdgcn_alignbit(T[0][ii], win[0], rp_width(pe));
-          win[1] = __builtin_amdgcn_alignbit(T[1][ii], win[1], rp_width(pe));
+          const uint32_t t0 = __float_as_uint(S.get(0, ii)), t1 = __float_as_uint(S.get(1, ii));
+          o[0] = __builtin_amdgcn_alignbit(t0, win[0], rp_pack_shift(pe));
+          o[64] = __builtin_amdgcn_alignbit(t1, win[1], rp_pack_shift(pe));
+          win[0] = __builtin_amdgcn_alignbit(t0, win[0], rp_width(pe));
+          win[1] = __builtin_amdgcn_alignbit(t1, win[1], rp_width(pe));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1401,11 +1432,12 @@ k_rows(const LaunchArgs P) {
       for (int ii = 0; ii < 64; ++ii) {
         const uint32_t pe = row_lane(xs_v, ii);
         const uint32_t off = (rp_base(pe) >> 4) + (pe & 31u);   // stream bit of the field in this half
+        const uint32_t t0 = __float_as_uint(S.get(0, ii)), t1 = __float_as_uint(S.get(1, ii));
         if ((fp32_rows >> ii) & 1u) {   // an FP32 row: its two 16-bit halves in turn
-          append_field(codes, l, win, T[0][ii], T[1][ii], off, 16u);
-          append_field(codes, l, win, T[0][ii] >> 16, T[1][ii] >> 16, off + 16u, 16u);
+          append_field(codes, l, win, t0, t1, off, 16u);
+          append_field(codes, l, win, t0 >> 16, t1 >> 16, off + 16u, 16u);
         } else {
-          append_field(codes, l, win, T[0][ii], T[1][ii], off, rp_width(pe));
+          append_field(codes, l, win, t0, t1, off, rp_width(pe));
         }
       }
     }

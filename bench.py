@@ -152,15 +152,20 @@ def fp32_comparator(cfg, f32_pool, inputs, o, reps: int = 4):
             "state": "fp32, 64 KiB per head, same kernel family (whole-head FP32 kind)"}
 
 
-def fp32_trajectory_error(cid: int):
+def fp32_trajectory_error(cid: int, fit_iters: int | None = None):
     """Error of the quantised decode trajectory against the unquantised delta
     rule on the same inputs: config `cid`'s pool and an FP32-kind pool start
     from the same state (the FP32 warm-up packed, or zero) and take the
     config's decode steps; relative L2 of the readouts over all steps and of
-    the final states (the quantised one restored by qdr_unpack)."""
+    the final states (the quantised one restored by qdr_unpack).  fit_iters
+    overrides the config's column fit (0: clip-free range, 1: least-squares
+    refit)."""
+    import dataclasses
     import torch
     from quantized_delta_rule_decode_amd import qdr, synth, workload
     cfg = synth.CONFIGS[cid]
+    if fit_iters is not None:
+        cfg = dataclasses.replace(cfg, fit_iters=fit_iters)
     tables = synth.static_tables(cfg)
     dev = torch.device("cuda")
     pool = workload.make_pool(cfg, tables)
@@ -189,7 +194,8 @@ def fp32_trajectory_error(cid: int):
     assert pool.qdr_poll_device_error() == 0 and ref.qdr_poll_device_error() == 0
     pool.close()
     ref.close()
-    return {"workload": cfg.name, "steps": cfg.steps, "o_rel_l2": (num / den) ** 0.5, "final_state_rel_l2": st}
+    return {"workload": cfg.name, "steps": cfg.steps, "column_fit": "least-squares refit" if cfg.fit_iters else "clip-free range",
+            "o_rel_l2": (num / den) ** 0.5, "final_state_rel_l2": st}
 
 
 def two_stream_split(pool, slots, inputs, o, fused_ms: float, reps: int = 5):
@@ -293,6 +299,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--fit-iters", type=int, default=None, choices=(0, 1),
+                    help="column fit of the timed pool: 0 the clip-free range, 1 plus the least-squares refit "
+                         "(default: the workload's own)")
     ap.add_argument("--fp32-warmup-steps", type=int, default=None,
                     help="FP32 delta-rule steps that build the warm state (default: the config's)")
     ap.add_argument("--cpu-requests", type=int, default=64,
@@ -333,6 +342,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = synth.CONFIGS[args.config]
+    if args.fit_iters is not None:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, fit_iters=args.fit_iters)
     tables = synth.static_tables(cfg)
     dev = torch.device("cuda")
     t_setup = time.perf_counter()
@@ -380,7 +392,8 @@ def main():
     sc16 = None if args.no_split else compact_scales(cfg, tables, pool, slots, (q, k, v, beta, gate), o, gpu_ms)
     assert pool.qdr_poll_device_error() == 0
     stream = stream_reference()
-    traj = None if args.no_trajectory_error else [fp32_trajectory_error(c) for c in (1, 2, 3)]
+    traj = None if args.no_trajectory_error else \
+        [fp32_trajectory_error(1)] + [fp32_trajectory_error(c, f) for c in (2, 3) for f in (0, 1)]
     others = None if args.no_other_configs else other_configs()
     cpu = None
     if not args.no_cpu_baseline:

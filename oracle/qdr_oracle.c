@@ -196,7 +196,9 @@ void or_readout_magnitude(int d, const float *S, const float *q, float *m) {
  *   normal fp32); optional V1a (fit_iters = 1): for the codes chosen with V0,
  *   the exact weighted least-squares factor
  *     c_j = sum_i omega_i r_i S_ij zeta_ij / sum_i omega_i r_i^2 zeta_ij^2
- *   with zeta = z / q_i and omega_i r_i^2 = m_i, so the weights are m_i.
+ *   with zeta = z / q_i and omega_i r_i^2 = m_i, so the weights are m_i;
+ *   each sum is two fma chains, one per half of the rows, then added (order
+ *   not given by the pages: reading taken).
  * Codes: z_ij = nearest integer (ties to even) to the exact real product
  *   Y_ij * w_ij, where Y_ij = S_ij * (1/r_i) and w_ij = (1/c0_j) * q_i, each
  *   rounded to fp32.  |z| <= q_i always holds, so no clipping is needed.
@@ -277,7 +279,9 @@ void or_requant(int d, const uint8_t *kinds, const float *S,
       if (b16) c0 = or_bf16_up(c0);
     }
     float ec = 1.0f / c0;
-    float num = 0.0f, den = 0.0f;
+    /* refit sums: one fma chain over each half of the rows (rows 0..d/2-1
+     * and d/2..d-1, each ascending from +0), then the two halves added */
+    float num[2] = {0.0f, 0.0f}, den[2] = {0.0f, 0.0f};
     for (int i = 0; i < d; ++i) {
       int kind = kinds[i];
       if (!kind_is_int(kind)) continue;
@@ -287,13 +291,15 @@ void or_requant(int d, const uint8_t *kinds, const float *S,
       double z = rint((double)y * (double)w);   /* exact product, then RNE */
       e[i * d + j] = (uint32_t)(int32_t)z;
       if (fit_iters > 0) {
+        const int half = i < d / 2 ? 0 : 1;
         float zeta = (float)z * (1.0f / q);
         float p = m[i] * zeta;
-        num = fmaf(p, y, num);
-        den = fmaf(p, zeta, den);
+        num[half] = fmaf(p, y, num[half]);
+        den[half] = fmaf(p, zeta, den[half]);
       }
     }
-    c[j] = (fit_iters > 0 && den > 0.0f) ? num / den : c0;
+    const float num_all = num[0] + num[1], den_all = den[0] + den[1];
+    c[j] = (fit_iters > 0 && den_all > 0.0f) ? num_all / den_all : c0;
     if (b16 && fit_iters > 0) c[j] = or_bf16_nearest(c[j]);
   }
   if (m_out) memcpy(m_out, m, sizeof(float) * (size_t)d);

@@ -826,25 +826,13 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
         }
         __syncthreads();
         if (w == 1) {
+          // each wave summed its own rows; the halves are added in row order
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            float nn = sh.d[l + 64 * c], dd = sh.y[l + 64 * c];
-#pragma unroll
-            for (int i4 = 0; i4 < 16; ++i4) {
-              const float4 m4 = lds4(&sh.m[64 + 4 * i4]);
-              const float mm[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float t = __builtin_fmaf(S.get(c, 4 * i4 + e), wq[c], kMagic);
-                const float zeta = (t - kMagic) * INVQ;
-                const float pz = mm[e] * zeta;
-                nn = __builtin_fmaf(pz, S.get(c, 4 * i4 + e), nn);
-                dd = __builtin_fmaf(pz, zeta, dd);
-              }
-            }
+            const float nn = sh.d[l + 64 * c] + nacc[c], dd = sh.y[l + 64 * c] + dacc[c];
             float cf = (dd > 0.0f) ? rn_div(nn, dd) : c0[c];
             if constexpr (SC16) cf = bf16_nearest(cf);
-            store_sc<SC16>(rs, cf, (uint32_t)l + 64u * c, c_off);
+            store_sc<SC16>(rs, cf, lane_now() + 64u * c, c_off);
           }
         }
       }
@@ -1338,14 +1326,9 @@ k_rows(const LaunchArgs P) {
   // or fp32 of S) in LDS; P1 turns every value into its code bits in place
   // (straight-line); P2 appends each row's field to the column windows in
   // row order and stores every completed word.
-  // V1a refit sums: fma chains over the integer rows in ascending order, so
-  // wave 1 starts from wave 0's totals over rows 0..63 (it waits for them)
+  // V1a refit sums: each wave runs an fma chain over its own integer rows in
+  // ascending order; wave 1 adds wave 0's sums to its own at the end
   float nacc[2] = {0.0f, 0.0f}, dacc[2] = {0.0f, 0.0f};
-  if (FIT && dual(SCALE) && w == 1) {
-    __syncthreads();
-    nacc[0] = sh.d[l]; nacc[1] = sh.d[l + 64];
-    dacc[0] = sh.y[l]; dacc[1] = sh.y[l + 64];
-  }
   // code bits replace the values in place (the tile holds the bit patterns)
   row_groups<kAhead>(&sh.qm[64 * w], [&](int i4, const float4 q4) {
     const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
@@ -1371,9 +1354,11 @@ k_rows(const LaunchArgs P) {
       }
     }
   });
-  if (FIT && dual(SCALE) && w == 0) {
-    sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
-    sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];
+  if (FIT && dual(SCALE)) {
+    if (w == 0) {
+      sh.d[l] = nacc[0]; sh.d[l + 64] = nacc[1];
+      sh.y[l] = dacc[0]; sh.y[l + 64] = dacc[1];
+    }
     __syncthreads();
   }
   if (pivots != 0) {
@@ -1470,10 +1455,11 @@ k_rows(const LaunchArgs P) {
   // ---------------- refitted column factors
   if (FIT && dual(SCALE) && has_int) {
     if (w == 1) {
-      // wave 1 holds the sums over all integer rows
+      // wave 0's sums (rows 0..63) plus wave 1's (rows 64..127)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        float cf = (dacc[c] > 0.0f) ? rn_div(nacc[c], dacc[c]) : c0[c];
+        const float nn = sh.d[l + 64 * c] + nacc[c], dd = sh.y[l + 64 * c] + dacc[c];
+        float cf = (dd > 0.0f) ? rn_div(nn, dd) : c0[c];
         if constexpr (SC16) cf = bf16_nearest(cf);
         store_sc<SC16>(rs, cf, (uint32_t)l + 64u * c, c_off);
       }

@@ -51,6 +51,10 @@ class Config:
     warmup: int            # FP32 warmup steps before packing (0: zero state)
     outliers: bool         # outlier-column / outlier-key generators
     gate_mode: str         # "per_step", "per_head", "per_row"
+    # column fit: 0 the clip-free range; 1 plus the weighted least-squares
+    # refit, the fit of the pools that hold ternary (INT2) rows: with the
+    # clip-free range an INT2 code rounds [c/2, c) up to c at every step, and
+    # long-lived INT2 rows grow without bound
     fit_iters: int = 0
     device_inputs: bool = False
 
@@ -65,13 +69,13 @@ CONFIGS = {
     2: Config(2, "gdn_b32_h48_nominal6", 32, 48, 32, UNIT_HEAD, GATE_SCALAR,
               SCALE_DUAL, 1024, 0, True, "per_head"),
     3: Config(3, "kda_b128_h32_nominal4", 128, 32, 128, UNIT_ROW, GATE_DIAG,
-              SCALE_DUAL, 256, 0, False, "per_row"),
+              SCALE_DUAL, 256, 0, False, "per_row", fit_iters=1),
     4: Config(4, "gdn_pool_b512_h2304_nominal6", 512, 2304, 512, UNIT_HEAD,
               GATE_SCALAR, SCALE_DUAL, 1, 256, False, "per_step",
               device_inputs=True),
     5: Config(5, "kda_slots2561_b512_h1536_nominal4", 512, 1536, 5 * 512 + 1,
               UNIT_ROW, GATE_DIAG, SCALE_DUAL, 64, 0, True, "per_row",
-              device_inputs=True),
+              fit_iters=1, device_inputs=True),
 }
 
 

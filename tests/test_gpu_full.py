@@ -144,7 +144,7 @@ def test_config4_every_head_of_eight_requests(torch_dev, orc):
         del S
     # the checked requests: one host-generated dense state, packed by both sides
     ref = orc.Pool(n, cfg.H, t["kinds"], t["omega"], unit=cfg.unit, gate=cfg.gate,
-                   scale_mode=cfg.scale_mode).alloc()
+                   scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters).alloc()
     for i, r in enumerate(req):
         S = synth.random_state(40000 + int(r), 1, cfg.H)
         pool.qdr_pack(slots[r:r + 1].contiguous(), torch.from_numpy(S).cuda())
@@ -184,7 +184,7 @@ def test_config5_every_head_of_a_request(torch_dev, orc, request_index):
     slots = torch.from_numpy(t["slots"]).cuda()
     pool.qdr_slot_reset(slots)
     ref = orc.Pool(1, cfg.H, t["kinds"], t["omega"], unit=cfg.unit, gate=cfg.gate,
-                   scale_mode=cfg.scale_mode).alloc()
+                   scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters).alloc()
     ref.pack(np.array([0], np.int32), np.zeros((1, cfg.H, D, D), np.float32))
     view = _RequestSlots(pool, [t["slots"][r]])
     o = torch.empty((cfg.B, cfg.H, D), dtype=torch.float32, device="cuda")

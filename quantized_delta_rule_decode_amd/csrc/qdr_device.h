@@ -406,9 +406,8 @@ __device__ __forceinline__ void delta_update(Tile &S, const float (&dl)[2], cons
 }
 
 // Calls f(i4, x4) on the 16 float4 groups of a 64-entry per-row LDS table in
-// order, each group's read issued A groups before its use (the row-unit
-// kernel runs two waves per SIMD, too few to cover an LDS read issued one
-// group ahead).
+// order, each group's read issued A groups before its use (in the row-unit
+// kernel an LDS read issued in its own group's turn would stall its wave).
 template <int A, class F>
 __device__ __forceinline__ void row_groups(const float *t, F &&f) {
   float4 q[16];
@@ -967,10 +966,10 @@ __device__ __forceinline__ void append_field(uint32_t *out, int l, uint32_t (&wi
 // --------------------------------------------------------------------------
 template <int MODE, int GATE, int SCALE, int FIT>
 __global__ void __launch_bounds__(128)
-// two waves per SIMD: the row tables, the pivot bookkeeping and the LDS
-// addressing leave no room for the three-wave budget of 168 VGPRs (the
-// allocator spills there, which costs more than the third wave gains)
-__attribute__((amdgpu_waves_per_eu(2)))
+// three waves per SIMD (168 VGPRs): the third wave covers the LDS and memory
+// latency of the per-row extraction (config 5: 8.63 -> 6.86 ms with the
+// clip-free fit, 10.64 -> 8.06 ms with the refit, against two waves)
+__attribute__((amdgpu_waves_per_eu(3)))
 k_rows(const LaunchArgs P) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_codes[];   // 16-byte aligned: staged with ds_write_b128
   __shared__ SharedCore sh;
@@ -1022,8 +1021,9 @@ k_rows(const LaunchArgs P) {
   uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
   const uint32_t lane_byte = (uint32_t)l * 4u;                       // column l of word 0
   // rows (restore) and table groups (other passes) whose LDS reads are in
-  // flight ahead of their use; the refit's extra sums leave room for two
-  constexpr int kAhead = FIT ? 2 : 4;
+  // flight ahead of their use, within the three-wave register budget (the
+  // refit's extra sums leave room for one)
+  constexpr int kAhead = FIT ? 1 : 2;
   // ---------------- every load of the item goes out here, ahead of the
   // first wait: the row programs and row data, then the code chunks (the HBM
   // stream).  (Loads issued after a wait, or behind a branch on loaded data,

@@ -293,6 +293,50 @@ def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
             "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def calibration(kind: str, cid: int, launches: int = 3):
+    """Three launches of a kernel whose HBM bytes are known; prints them as
+    one JSON line.  rocprofv3's FETCH_SIZE / WRITE_SIZE per dispatch over
+    these bytes gives the factor its readings are scaled by (one copy and one
+    in-place pattern, and the decode step's own block loads and stores)."""
+    import torch
+    if kind in ("copy", "inplace"):
+        n = 4 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src) if kind == "copy" else None
+        for _ in range(launches):
+            if kind == "copy":
+                dst.copy_(src)
+            else:
+                src.add_(1.0)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": kind, "read_bytes": n, "write_bytes": n, "launches": launches,
+                          "kernel": "torch copy_" if kind == "copy" else "torch add_ (in place)"}), flush=True)
+        return
+    from quantized_delta_rule_decode_amd import synth, workload
+    cfg = synth.CONFIGS[cid]
+    tables = synth.static_tables(cfg)
+    B = 64
+    pool = workload.fp32_pool(cfg, B)
+    ident = torch.arange(B, dtype=torch.int32, device="cuda")
+    pool.qdr_slot_reset(ident)
+    sub = synth.Config(**{**cfg.__dict__, "B": B})
+    q, k, v, beta, gate = workload.step_inputs(sub, tables, 0)
+    o = torch.empty((B, cfg.H, 128), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        pool.qdr_decode_step(ident, q, k, v, beta, gate, o)
+    torch.cuda.synchronize()
+    assert pool.qdr_poll_device_error() == 0
+    heads = B * cfg.H
+    block = 128 * 128 * 4
+    vec_in = 3 * 128 * 4 + 4 + (4 if cfg.gate == 0 else 4 * 128)
+    print(json.dumps({"calibration": kind, "workload": cfg.name, "requests": B, "heads": heads,
+                      "read_bytes": heads * (block + vec_in), "write_bytes": heads * (block + 128 * 4),
+                      "block_bytes_each_way": heads * block, "launches": launches,
+                      "kernel": "k_head<32, ...> (FP32-kind decode step)"}), flush=True)
+    pool.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,18 +362,15 @@ def main():
                     help="skip timing configs 1, 2, 3 and 5 next to the benchmark configuration")
     ap.add_argument("--cpu-requests-single", type=int, default=2,
                     help="requests in the single-threaded oracle sample (2 x 2304 heads: about 10 s)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--calibration", choices=("copy", "inplace", "fp32pool"), default=None,
+                    help="only run a kernel of known HBM bytes (calibrates rocprofv3's byte counters): "
+                         "copy = a 4 GiB device copy, inplace = torch add_ on 4 GiB (read, then written "
+                         "in place), fp32pool = the decode step on an FP32-kind pool of 64 requests x "
+                         "the config's heads (each 64 KiB block read and written back in place by the "
+                         "step's own buffer loads and stores)")
     args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
-        n = args.copy_calibration << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 3}), flush=True)
+    if args.calibration:
+        calibration(args.calibration, args.config)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode step has no "

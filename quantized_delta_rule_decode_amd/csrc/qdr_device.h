@@ -537,10 +537,18 @@ struct Shared : SharedCore {
 // Waves per SIMD the register allocation targets: three for the dual-axis
 // integer kernels (their 128-register tile plus working set fits in 168
 // VGPRs), two where it does not (float kinds, the refit variant, the
-// row-absmax baseline).
+// row-absmax baseline, and the write-back of the two-launch step, which
+// restores the state a second time next to its first readout and spilled
+// over 200 registers at the three-wave budget).
 template <int BITS, int MODE, int SCALE, int FIT>
 struct Occupancy {
-  static constexpr int waves = (BITS <= 8 && FIT == 0 && dual(SCALE)) ? 3 : 2;
+  static constexpr int waves = (BITS <= 8 && FIT == 0 && dual(SCALE) && MODE != MODE_WRITEBACK) ? 3 : 2;
+};
+// The row-unit kernel: three waves per SIMD except the write-back (about 100
+// registers over the three-wave budget) and the pack of dense states (up to 9).
+template <int MODE>
+struct RowsOccupancy {
+  static constexpr int waves = (MODE == MODE_WRITEBACK || MODE == MODE_PACK) ? 2 : 3;
 };
 
 // The work of one (request b, head h) of kind BITS; sh is the workgroup's
@@ -969,7 +977,7 @@ __global__ void __launch_bounds__(128)
 // three waves per SIMD (168 VGPRs): the third wave covers the LDS and memory
 // latency of the per-row extraction (config 5: 8.63 -> 6.86 ms with the
 // clip-free fit, 10.64 -> 8.06 ms with the refit, against two waves)
-__attribute__((amdgpu_waves_per_eu(3)))
+__attribute__((amdgpu_waves_per_eu(RowsOccupancy<MODE>::waves)))
 k_rows(const LaunchArgs P) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_codes[];   // 16-byte aligned: staged with ds_write_b128
   __shared__ SharedCore sh;

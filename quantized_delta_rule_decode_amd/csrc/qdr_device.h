@@ -919,7 +919,7 @@ __device__ __forceinline__ uint32_t row_lane(uint32_t xs_v, int i) {
 }
 // fields of a program word: LDS byte offset of the field's first word, the
 // width of a 2..16-bit field, the repack's completing shift (low 5 bits)
-__device__ __forceinline__ uint32_t rp_base(uint32_t e) { return e & ~511u; }
+__device__ __forceinline__ uint32_t rp_base(uint32_t e) { return e & (kRowCompletes - 512u); }
 __device__ __forceinline__ uint32_t rp_width(uint32_t e) { return (e >> 4) & 30u; }
 __device__ __forceinline__ uint32_t rp_pack_shift(uint32_t e) { return 0u - e; }
 
@@ -1389,10 +1389,10 @@ k_rows(const LaunchArgs P) {
     // read), then out with 16-byte stores, 1 KiB of the half per instruction
     uint32_t win[2] = {0u, 0u};   // the last 32 stream bits written, per column
     if (fp32_rows == 0) {
-      // every field is at most 16 bits wide: straight-line appends.  The word
-      // a field ends in is written whether or not the field completes it; a
-      // word that is not yet complete is rewritten by the field that
-      // completes it (or by the final flush), later in program order.
+      // every field is at most 16 bits wide: straight-line appends; a field
+      // that completes its word (the program word's flag, a uniform branch)
+      // also writes that word.  A word left incomplete by the last field is
+      // written by the final flush.
       // this pass reads no LDS, so the program words come in by scalar loads
       // (constant address space), eight rows per load, one batch ahead,
       // instead of a v_readlane per row
@@ -1411,10 +1411,12 @@ k_rows(const LaunchArgs P) {
         for (int e = 0; e < 8; ++e) {
           const int ii = 8 * b8 + e;
           const uint32_t pe = pb[b8 & 1][e];
-          uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
           const uint32_t t0 = __float_as_uint(S.get(0, ii)), t1 = __float_as_uint(S.get(1, ii));
-          o[0] = __builtin_amdgcn_alignbit(t0, win[0], rp_pack_shift(pe));
-          o[64] = __builtin_amdgcn_alignbit(t1, win[1], rp_pack_shift(pe));
+          if (pe & kRowCompletes) {
+            uint32_t *o = reinterpret_cast<uint32_t *>(codes8 + (rp_base(pe) | lane_byte));
+            o[0] = __builtin_amdgcn_alignbit(t0, win[0], rp_pack_shift(pe));
+            o[64] = __builtin_amdgcn_alignbit(t1, win[1], rp_pack_shift(pe));
+          }
           win[0] = __builtin_amdgcn_alignbit(t0, win[0], rp_width(pe));
           win[1] = __builtin_amdgcn_alignbit(t1, win[1], rp_width(pe));
         }

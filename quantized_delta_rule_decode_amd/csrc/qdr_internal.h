@@ -40,13 +40,16 @@ static_assert(sizeof(HeadInfo) == 16 && sizeof(ListEntry) == 32, "device table l
 // low 9 bits are zero), y = bit offset of the field in that word and
 // z = the field's width (the row's kind).  One word serves the restore and
 // the repack:
-//   xs = x | (z / 2) << 5 | y   (z / 2 in 1..8 for the 2..16-bit kinds, 0 for FP32)
+//   xs = x | (z / 2) << 5 | y | c << 30   (z / 2 in 1..8 for the 2..16-bit
+//   kinds, 0 for FP32; c = 1 when a 2..16-bit field reaches the end of its
+//   first word, y + z >= 32)
 // The restore's funnel shift by y and the repack's completing shift by
 // (32 - y) & 31 = (-xs) & 31 read only the low 5 bits of their operand;
 // (xs >> 4) & 30 is the width of a 2..16-bit field; the LDS address is x
-// with the low 9 bits replaced by the lane's byte.
+// (bits 9..29) with the low 9 bits replaced by the lane's byte.
+constexpr uint32_t kRowCompletes = 1u << 30;   // c above
 struct RowProg {
-  uint32_t xs;   // x | width code | shift
+  uint32_t xs;   // x | width code | shift | completes
   uint32_t z;    // width
 };
 

@@ -134,7 +134,8 @@ void build_layout(const qdr_pool_desc *d, HostLayout &L) {
         if (d->unit == QDR_UNIT_ROW) {
           const uint32_t x = (uint32_t)(hbits >> 5) * (QDR_DIM * 4u), y = (uint32_t)(hbits & 31u);
           const uint32_t wcode = k == 32 ? 0u : (uint32_t)k / 2u;
-          L.row_prog[(size_t)h * QDR_DIM + i] = {x | (wcode << 5) | y, (uint32_t)k};
+          const uint32_t completes = (k != 32 && y + (uint32_t)k >= 32u) ? qdr::kRowCompletes : 0u;
+          L.row_prog[(size_t)h * QDR_DIM + i] = {x | (wcode << 5) | y | completes, (uint32_t)k};
         }
         hbits += (uint64_t)k;
         any_int = any_int || is_int_kind(k);

@@ -410,16 +410,19 @@ def main():
     for _ in range(args.warmup):
         pool.qdr_decode_step(slots, q, k, v, beta, gate, o)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    # one event between consecutive steps: the first and last bracket the K
+    # timed steps (their mean is ms_per_step), the others give each step's
+    # own time for the median, min and max
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         pool.qdr_decode_step(slots, q, k, v, beta, gate, o)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    gpu_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     assert pool.qdr_poll_device_error() == 0
 
     nbytes = algorithmic_bytes(cfg, tables)
@@ -457,6 +460,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": gpu_ms,
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": per_step[0],
+        "ms_per_step_max": per_step[-1],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

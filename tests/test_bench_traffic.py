@@ -34,3 +34,19 @@ def test_traffic_withheld_for_an_unprofiled_workload(monkeypatch):
     rec = _record()
     monkeypatch.setattr(build, "device_source_hash", lambda: rec["kernel_source_sha256_16"])
     assert bench.measured_traffic(99) is None
+
+
+def test_algorithmic_bytes_of_the_gdn_pool():
+    """The benchmark pool's bytes per step, written out from its head counts
+    and the per-head sizes of each kind: 128 x 128 codes of b bits (FP16
+    pivots 32 KiB), fp32 r and c (1 KiB) for integer heads, each read and
+    written once, plus q, k, v, beta, the scalar gate and o per head-step."""
+    from quantized_delta_rule_decode_amd import synth
+    cfg = synth.CONFIGS[4]
+    counts = {16: 46, 8: 691, 6: 991, 4: 576}
+    codes = sum(n * 128 * 128 * b // 8 for b, n in counts.items())
+    scales = sum(n for b, n in counts.items() if b <= 8) * 2 * 128 * 4
+    vectors = cfg.H * (3 * 128 * 4 + 4 + 4 + 128 * 4)
+    per_request = 2 * (codes + scales) + vectors
+    assert per_request * cfg.B == 35_231_105_024
+    assert bench.algorithmic_bytes(cfg, synth.static_tables(cfg)) == per_request * cfg.B

@@ -29,11 +29,13 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "state-update steps/s (requests x heads) at B=512, 6-bit; achieved HBM GB/s"
 
 
-def algorithmic_bytes(cfg, tables, scale_bits: int = 32) -> int:
+def algorithmic_bytes(cfg, tables, scale_bits: int = 32, integer_heads_only: bool = False) -> int:
     """Bytes one step must move by the method's own accounting: every code
     (b bits per state value of its row, no layout padding) and every scale
     (scale_bits wide) read and written once, q/k/v, beta and the gate read,
-    o written."""
+    o written.  integer_heads_only: only the head-steps of the dominant launch
+    (whole-head pools: the integer heads, which k_head_int takes; row-unit
+    pools: every head, all in the one k_rows launch)."""
     H = cfg.H
     kinds = np.asarray(tables["kinds"], np.int64)
     rows = np.repeat(kinds, 128).reshape(H, 128) if cfg.unit == 0 else kinds.reshape(H, 128)
@@ -41,14 +43,24 @@ def algorithmic_bytes(cfg, tables, scale_bits: int = 32) -> int:
     has_int = (rows <= 8).any(axis=1)
     scales = np.where(has_int, (2 if cfg.scale_mode == 0 else 1) * 128 * scale_bits // 8, 0)
     gate_bytes = 4 if cfg.gate == 0 else 4 * 128
-    per_req = int((2 * code + 2 * scales).sum()) + H * (3 * 128 * 4 + 4 + gate_bytes + 128 * 4)
+    vec = 3 * 128 * 4 + 4 + gate_bytes + 128 * 4
+    take = (rows <= 8).all(axis=1) if (integer_heads_only and cfg.unit == 0) else np.ones(H, bool)
+    per_req = int((2 * code + 2 * scales + vec)[take].sum())
     return per_req * cfg.B
 
 
-def measured_traffic(cid: int):
+def dominant_kernel(cfg) -> str:
+    """rocprofv3's name of the step's dominant launch (template arguments:
+    mode, gate, scale mode, column fit)."""
+    name = "k_head_int" if cfg.unit == 0 else "k_rows"
+    return f"void qdr::{name}<0, {cfg.gate}, {cfg.scale_mode}, {1 if cfg.fit_iters else 0}>(qdr::LaunchArgs)"
+
+
+def measured_traffic(cid: int, kernel: str | None = None):
     """HBM bytes per step from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    runs (scaled by a plain-copy calibration), or None when the kernel source
-    has changed since those counters were taken."""
+    runs (scaled by the calibration of those counters): of the whole step, or
+    of one kernel's launch.  None when the kernel sources have changed since
+    those counters were taken, or nothing was recorded for the workload."""
     from quantized_delta_rule_decode_amd.build import device_source_hash
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -59,7 +71,10 @@ def measured_traffic(cid: int):
     entry = rec.get(f"config{cid}")
     if rec.get("kernel_source_sha256_16") != sha or entry is None:
         return None
-    return entry["fetch_bytes_per_step"] + entry["write_bytes_per_step"]
+    if kernel is None:
+        return entry["fetch_bytes_per_step"] + entry["write_bytes_per_step"]
+    k = entry.get("kernel_bytes", {}).get(kernel)
+    return None if k is None else k["fetch"] + k["write"]
 
 
 def cpu_baseline(cfg, tables, requests: int, threads: int):
@@ -426,10 +441,16 @@ def main():
     assert pool.qdr_poll_device_error() == 0
 
     nbytes = algorithmic_bytes(cfg, tables)
-    traffic = measured_traffic(cfg.cid)
     head_steps = cfg.B * cfg.H
-    achieved = nbytes / (gpu_ms * 1e-3) / 1e9
+    achieved_step = nbytes / (gpu_ms * 1e-3) / 1e9
     value = head_steps / (gpu_ms * 1e-3)
+    # the roofline of the dominant launch: its own head-steps' bytes over its
+    # duration, which is the step time (it is launched on the caller's stream
+    # and spans the step; the float-kind launch runs inside it)
+    kernel = dominant_kernel(cfg)
+    kbytes = algorithmic_bytes(cfg, tables, integer_heads_only=True)
+    achieved = kbytes / (gpu_ms * 1e-3) / 1e9
+    traffic = measured_traffic(cfg.cid, kernel)
 
     split = None if args.no_split else two_stream_split(pool, slots, (q, k, v, beta, gate), o, gpu_ms)
     bf16_io = None if args.no_split else compact_io(cfg, tables, pool, slots, (q, k, v, beta, gate), gpu_ms)
@@ -472,18 +493,23 @@ def main():
                    "mean_code_bits": round(float(np.mean(tables["kinds"])), 3),
                    "stored_bits_per_value": round(pool.bits_per_value, 3),
                    "fp32_warmup_steps": warm},
-        "achieved_GBps": achieved,
+        "achieved_GBps": achieved_step,
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "unit_of_work": ("one qdr_decode_step: whole-head pools launch k_head_int over every "
-                                      "integer head (the dominant kernel) and, on a second stream forked "
-                                      "from and joined back to the caller's, one launch per float kind; "
-                                      "row-unit pools launch k_rows once; achieved = algorithmic bytes per "
-                                      "step / step time (HIP events on the caller's stream)"),
-                     "traffic_over_algorithmic": None if traffic is None else traffic / nbytes,
+                     "kernel": kernel, "algorithmic_bytes_per_launch": kbytes,
+                     "launch_ms": gpu_ms,
+                     "unit_of_work": ("one launch of the dominant kernel per decode step: whole-head pools "
+                                      "launch k_head_int over every integer head and, on a second stream "
+                                      "forked from and joined back to the caller's, one launch per float "
+                                      "kind, which runs inside the integer launch's span; row-unit pools "
+                                      "launch k_rows once.  achieved = the launch's algorithmic bytes (its "
+                                      "head-steps x their bytes per head-step) / its duration, the step "
+                                      "time of HIP events on the caller's stream, the launch's own stream; "
+                                      "achieved_GBps at the top counts every head of the step"),
+                     "traffic_over_algorithmic": None if traffic is None else traffic / kbytes,
                      "stream_reference": stream,
-                     "frac_of_stream_reference": achieved / stream["GBps"]},
+                     "frac_of_stream_reference": achieved_step / stream["GBps"]},
         "fp32_state_comparator": None if fp32_cmp is None else {
             **fp32_cmp, "speedup_packed_over_fp32": fp32_cmp["ms_per_step"] / gpu_ms},
         "two_stream_split": split,

@@ -297,6 +297,26 @@ def compact_scales(cfg, tables, pool, slots, inputs, o, fused_ms: float, reps: i
     return out
 
 
+def batch_sweep(cfg, tables, pool, slots, inputs, o, batches=(32, 64, 128, 256), reps: int = 10):
+    """The same pool stepped for the first b requests only, for each b: the
+    decode-step throughput over batch sizes (the pages time the whole step
+    at batches from 32 to 512: Review (singularity-lens), throughput
+    paragraph).  Every step is one qdr_decode_step on the same inputs."""
+    import dataclasses
+    out = []
+    for b in batches:
+        if b >= cfg.B:
+            continue
+        sub = dataclasses.replace(cfg, B=b)
+        ins = tuple(x[:b] for x in inputs)
+        ms = time_on_stream(lambda: pool.qdr_decode_step(slots[:b], *ins, o[:b]), reps, warmup=2)
+        nbytes = algorithmic_bytes(sub, tables)
+        out.append({"B": b, "ms_per_step": ms, "state_update_steps_per_s": b * cfg.H / (ms * 1e-3),
+                    "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac_of_peak_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    return out
+
+
 def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
     """HBM rate of a plain in-place streaming kernel on this GPU (torch add_ of
     an fp32 buffer: each byte read once and written once), for scale."""
@@ -373,6 +393,8 @@ def main():
                          "bfloat16-scale pool")
     ap.add_argument("--no-trajectory-error", action="store_true",
                     help="skip the quantised-vs-FP32 trajectory error of the small configs")
+    ap.add_argument("--no-batch-sweep", action="store_true",
+                    help="skip timing the step on the first 32, 64, 128 and 256 requests of the pool")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip timing configs 1, 2, 3 and 5 next to the benchmark configuration")
     ap.add_argument("--cpu-requests-single", type=int, default=2,
@@ -459,6 +481,8 @@ def main():
     stream = stream_reference()
     traj = None if args.no_trajectory_error else \
         [fp32_trajectory_error(1)] + [fp32_trajectory_error(c, f) for c in (2, 3) for f in (0, 1)]
+    sweep = None if args.no_batch_sweep else batch_sweep(cfg, tables, pool, slots, (q, k, v, beta, gate), o)
+    assert pool.qdr_poll_device_error() == 0
     others = None if args.no_other_configs else other_configs()
     cpu = None
     if not args.no_cpu_baseline:
@@ -516,6 +540,7 @@ def main():
         "bf16_io_step": bf16_io,
         "bf16_scales_step": sc16,
         "fp32_trajectory_error": traj,
+        "batch_sweep": sweep,
         "other_configs": others,
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,

@@ -523,6 +523,8 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "kernel": kernel, "algorithmic_bytes_per_launch": kbytes,
                      "launch_ms": gpu_ms,
+                     "whole_step": {"algorithmic_bytes": nbytes, "achieved": achieved_step,
+                                    "frac": achieved_step / PEAK_HBM_GBPS},
                      "unit_of_work": ("one launch of the dominant kernel per decode step: whole-head pools "
                                       "launch k_head_int over every integer head and, on a second stream "
                                       "forked from and joined back to the caller's, one launch per float "

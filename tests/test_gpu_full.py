@@ -3,8 +3,10 @@
 Config 4 is the benchmark's own launch: the 512 x 2304-head GDN pool, one
 quantised decode step over every request.  Two checks: every head of eight
 requests (0 and 511 among them) from a dense state generated on the host,
-which both sides pack; and sampled heads of the benchmark's own warm state
-(256 FP32 decode steps, then pack).  Config 5 is the (5B+1)-slot KDA pool
+which both sides pack; the same for three requests under each step variant
+the benchmark also times (bfloat16 factors, bfloat16 I/O, the two-launch
+step); and sampled heads of the benchmark's own warm state (256 FP32 decode
+steps, then pack).  Config 5 is the (5B+1)-slot KDA pool
 with a random slot map, 64 decode steps from the zero state over all 512
 requests, every head of one request per case checked at every step.  The
 oracle gets the same seeded inputs (copied from the device generator) and
@@ -125,13 +127,16 @@ def _host_rows(inputs, req):
     return tuple(np.ascontiguousarray(x[req].cpu().numpy()) for x in inputs)
 
 
-def test_config4_every_head_of_eight_requests(torch_dev, orc):
-    torch = torch_dev
+def _config4_checked_pool(torch, orc, req, scale_bits=32):
+    """The benchmark pool with random device-packed states in every slot and,
+    in the slots of the checked requests, one host-generated dense state that
+    both sides pack (so the oracle never takes a device byte).  Returns the
+    config, its tables, the pool, the device slot map, the oracle pool of the
+    checked requests and the device pool seen through their slots."""
     cfg = synth.CONFIGS[4]
     t = synth.static_tables(cfg)
-    req = np.array([0, 73, 146, 219, 292, 365, 438, 511])
     n = req.size
-    pool = workload.make_pool(cfg, t)
+    pool = workload.make_pool(cfg, t, scale_bits=scale_bits)
     slots = torch.from_numpy(t["slots"]).cuda()
     # the other requests: random dense states generated and packed on the device
     gen = torch.Generator(device="cuda")
@@ -144,7 +149,7 @@ def test_config4_every_head_of_eight_requests(torch_dev, orc):
         del S
     # the checked requests: one host-generated dense state, packed by both sides
     ref = orc.Pool(n, cfg.H, t["kinds"], t["omega"], unit=cfg.unit, gate=cfg.gate,
-                   scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters).alloc()
+                   scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters, scale_bits=scale_bits).alloc()
     for i, r in enumerate(req):
         S = synth.random_state(40000 + int(r), 1, cfg.H)
         pool.qdr_pack(slots[r:r + 1].contiguous(), torch.from_numpy(S).cuda())
@@ -155,7 +160,16 @@ def test_config4_every_head_of_eight_requests(torch_dev, orc):
     for i in range(n):
         assert np.array_equal(view.qdr_read_raw(i), ref.mem[i * ref.slot_stride:(i + 1) * ref.slot_stride]), \
             f"packed state of request {req[i]} differs"
-    print(f"config 4: packed states of requests {req.tolist()} match ({n} x {cfg.H} heads)", flush=True)
+    print(f"config 4 (scale bits {scale_bits}): packed states of requests {req.tolist()} match "
+          f"({n} x {cfg.H} heads)", flush=True)
+    return cfg, t, pool, slots, ref, view
+
+
+def test_config4_every_head_of_eight_requests(torch_dev, orc):
+    torch = torch_dev
+    req = np.array([0, 73, 146, 219, 292, 365, 438, 511])
+    n = req.size
+    cfg, t, pool, slots, ref, view = _config4_checked_pool(torch, orc, req)
     ins = workload.step_inputs(cfg, t, 0)
     o = torch.empty((cfg.B, cfg.H, D), dtype=torch.float32, device="cuda")
     pool.qdr_decode_step(slots, *ins, o)
@@ -171,6 +185,59 @@ def test_config4_every_head_of_eight_requests(torch_dev, orc):
     parity.assert_step_ok(rep, "config 4 decode step")
     print(f"config 4: every head of {n} requests matches after the step: o rel L2 {rep.o_rel_l2:.2e}, "
           f"worst head {rep.o_worst_head:.2e}, excused codes {rep.codes_excused}", flush=True)
+    pool.close()
+
+
+# The step variants the benchmark line times on the same pool: bfloat16 scale
+# factors, bfloat16 q/k/v/o, and the two-launch (readout, then write-back)
+# step.  Every head of three requests against the oracle, at full size.
+@pytest.mark.parametrize("variant", ["bf16_scales", "bf16_io", "split"])
+def test_config4_step_variants_every_head(torch_dev, orc, variant):
+    torch = torch_dev
+    req = np.array([0, 255, 511])
+    n = req.size
+    cfg, t, pool, slots, ref, view = _config4_checked_pool(
+        torch, orc, req, scale_bits=16 if variant == "bf16_scales" else 32)
+    q, k, v, beta, gate = workload.step_inputs(cfg, t, 0)
+    o = torch.empty((cfg.B, cfg.H, D), dtype=torch.float32, device="cuda")
+    if variant == "bf16_io":
+        q16, k16, v16 = (x.to(torch.bfloat16) for x in (q, k, v))
+        o16 = torch.empty((cfg.B, cfg.H, D), dtype=torch.bfloat16, device="cuda")
+        pool.qdr_decode_step_bf16(slots, q16, k16, v16, beta, gate, o16)
+        q, k, v = (x.float() for x in (q16, k16, v16))      # the widened inputs, exact
+    elif variant == "split":
+        s_read, s_wb = torch.cuda.Stream(), torch.cuda.Stream()
+        s_read.wait_stream(torch.cuda.current_stream())
+        s_wb.wait_stream(torch.cuda.current_stream())
+        pool.qdr_decode_step_split(slots, q, k, v, beta, gate, o, stream_readout=s_read, stream_writeback=s_wb)
+    else:
+        pool.qdr_decode_step(slots, q, k, v, beta, gate, o)
+    torch.cuda.synchronize()
+    assert pool.qdr_poll_device_error() == 0
+    sub = _host_rows((q, k, v, beta, gate), req)
+    prev = ref.mem.copy()
+    rslots = np.arange(n, dtype=np.int32)
+    o_ref, bad = ref.step(rslots, *sub, threads=16)
+    assert bad == 0
+    rep = parity.StepReport()
+    if variant == "bf16_io":
+        # o is the readout rounded to bfloat16: within half a bfloat16 step
+        # (at most 2^-8 of the value: 8 significant bits) of the oracle's,
+        # plus the readout's own bound
+        o_dev = o16.float().cpu().numpy()[req].reshape(-1, D).astype(np.float64)
+        o_r = np.asarray(o_ref, np.float64).reshape(-1, D)
+        mag = np.asarray(ref.last_o_mag, np.float64).reshape(-1, D)
+        err = np.abs(o_dev - o_r)
+        bound = 2.0 ** -8 * np.abs(o_r) + parity.O_WORST_HEAD * (
+            np.linalg.norm(o_r, axis=1, keepdims=True) + parity.MAG_WEIGHT * np.linalg.norm(mag, axis=1, keepdims=True))
+        assert np.all(err <= bound), f"bf16 readout: worst excess {np.max(err - bound):.3e}"
+        print(f"config 4 bf16_io: readout within {np.max(err / bound):.2f} of its bound", flush=True)
+    else:
+        parity.compare_o(o.cpu().numpy()[req], o_ref, rep, ref.last_o_mag)
+    parity.compare_pool(orc, ref, view, rslots, parity.step_state_fn(orc, ref, prev, rslots, sub), rep)
+    parity.assert_step_ok(rep, f"config 4 {variant} step")
+    print(f"config 4 {variant}: every head of {n} requests matches after the step "
+          f"(excused codes {rep.codes_excused})", flush=True)
     pool.close()
 
 

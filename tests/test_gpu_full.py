@@ -241,10 +241,15 @@ def test_config4_step_variants_every_head(torch_dev, orc, variant):
     pool.close()
 
 
-@pytest.mark.parametrize("request_index", [0, 170, 341, 511])
-def test_config5_every_head_of_a_request(torch_dev, orc, request_index):
+# Config 5 runs its least-squares refit; the clip-free column factor (the
+# row kernel's other instantiation) is checked on one request as well.
+@pytest.mark.parametrize("request_index,fit_iters", [(0, None), (170, None), (341, None), (511, None), (511, 0)])
+def test_config5_every_head_of_a_request(torch_dev, orc, request_index, fit_iters):
+    import dataclasses
     torch = torch_dev
     cfg = synth.CONFIGS[5]
+    if fit_iters is not None:
+        cfg = dataclasses.replace(cfg, fit_iters=fit_iters)
     t = synth.static_tables(cfg)
     r = int(request_index)
     pool = workload.make_pool(cfg, t)
@@ -274,7 +279,7 @@ def test_config5_every_head_of_a_request(torch_dev, orc, request_index):
         if s % 16 == 15:
             print(f"config 5 request {r} (slot {t['slots'][r]}): {s + 1} steps match", flush=True)
     assert pool.qdr_poll_device_error() == 0
-    print(f"config 5 request {r}: {cfg.steps} steps x {cfg.H} heads: worst o rel L2 {worst:.2e}, "
+    print(f"config 5 request {r} (fit {cfg.fit_iters}): {cfg.steps} steps x {cfg.H} heads: worst o rel L2 {worst:.2e}, "
           f"worst head {worst_head:.2e}, excused codes {excused}", flush=True)
     # slots outside the slot map were never touched (zero-filled at creation)
     unmapped = sorted(set(range(cfg.num_slots)) - set(t["slots"].tolist()))

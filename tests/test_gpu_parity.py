@@ -216,13 +216,16 @@ def test_deterministic(torch_dev, orc):
 
 
 # ----------------------------------------------------------------- configs
-def trajectory(torch, orc, cid, steps, threads=16, sb=32, requests=None):
+def trajectory(torch, orc, cid, steps, threads=16, sb=32, requests=None, fit_iters=None):
     """Config `cid` for `steps` decode steps: the device steps the whole batch,
     the oracle the listed requests (every request holds every head, and
     request trajectories are independent); per step the readouts and the
     packed slots of those requests are compared."""
     from quantized_delta_rule_decode_amd import workload
     cfg = synth.CONFIGS[cid]
+    if fit_iters is not None:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, fit_iters=fit_iters)
     t = synth.static_tables(cfg)
     req = np.arange(cfg.B) if requests is None else np.asarray(sorted(set(int(r) for r in requests)))
     dev = workload.make_pool(cfg, t, scale_bits=sb)
@@ -292,6 +295,16 @@ def test_config1_trajectory(torch_dev, orc):
 def test_config2_trajectory_full_length(torch_dev, orc, sb):
     cfg = synth.CONFIGS[2]
     worst, excused = trajectory(torch_dev, orc, 2, cfg.steps, sb=sb, requests=[0, 13, cfg.B - 1])
+    assert worst <= 1e-4
+
+
+# the other column fit of configs 2 and 3 (the benchmark reports the FP32
+# trajectory error of both), at full length
+@pytest.mark.parametrize("cid,fit_iters", [(2, 1), (3, 0)])
+def test_trajectory_full_length_other_fit(torch_dev, orc, cid, fit_iters):
+    cfg = synth.CONFIGS[cid]
+    worst, excused = trajectory(torch_dev, orc, cid, cfg.steps, requests=[0, cfg.B // 2, cfg.B - 1],
+                                fit_iters=fit_iters)
     assert worst <= 1e-4
 
 

@@ -168,7 +168,10 @@ qdr_status qdr_unpack(qdr_pool *pool, const int32_t *slots, int32_t n,
  *   o = S_t^T q (before requantisation), then S_t is requantised into the
  *   slot in place.
  * q, k, v, o: [B][H][128] fp32; beta: [B][H]; gate: [B][H] (QDR_GATE_SCALAR,
- * linear alpha = exp(-g)) or [B][H][128] (QDR_GATE_DIAG, linear a_i). */
+ * linear alpha = exp(-g)) or [B][H][128] (QDR_GATE_DIAG, linear a_i).
+ * Inputs are not checked for NaN or infinity: such values propagate through
+ * the arithmetic of their own (request, head) -- its readout and its stored
+ * block -- and leave every other head and request untouched. */
 qdr_status qdr_decode_step(qdr_pool *pool, const int32_t *slots, int32_t B,
                            const float *q, const float *k, const float *v,
                            const float *beta, const float *gate, float *o,

@@ -168,3 +168,49 @@ def test_negative_sizes_and_raw_io_arguments(torch_dev):
     assert all(np.array_equal(a, b) for a, b in zip(snapshot(pool), before))
     assert pool.qdr_poll_device_error() == 0
     pool.close()
+
+
+def test_nonfinite_inputs_stay_in_their_head(torch_dev):
+    """NaN and infinity in the inputs are not guarded: they propagate through
+    their own (request, head) only.  The same step on a twin pool with clean
+    inputs gives identical bytes and readouts everywhere else."""
+    torch = torch_dev
+    kinds = (6, 8, 4, 16)
+    pools = [small_pool(num_slots=3, kinds=kinds) for _ in range(2)]
+    st = torch.tensor([2, 0, 1], dtype=torch.int32, device="cuda")
+    B, H = 3, len(kinds)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    S = torch.randn((3, H, D, D), generator=g, device="cuda")
+    for p in pools:
+        p.qdr_pack(torch.arange(3, dtype=torch.int32, device="cuda"), S)
+    clean = inputs(torch, B, H)
+    dirty = [x.clone() for x in clean]
+    dirty[2][1, 0, 5] = float("nan")       # v of request 1, head 0
+    dirty[0][2, 3, 7] = float("inf")       # q of request 2, head 3 (readout only)
+    dirty[1][0, 2, 9] = float("-inf")      # k of request 0, head 2
+    hit = {(1, 0), (2, 3), (0, 2)}
+    outs = []
+    for p, ins in zip(pools, (clean, dirty)):
+        o = torch.empty((B, H, D), device="cuda")
+        p.qdr_decode_step(st, *ins, o)
+        torch.cuda.synchronize()
+        assert p.qdr_poll_device_error() == 0
+        outs.append(o.cpu().numpy())
+    slot_of = st.cpu().numpy()
+    for b in range(B):
+        a, c = pools[0].qdr_read_raw(int(slot_of[b])), pools[1].qdr_read_raw(int(slot_of[b]))
+        for h in range(H):
+            if (b, h) in hit:
+                continue
+            assert np.array_equal(outs[0][b, h], outs[1][b, h]), f"readout of request {b} head {h}"
+            off, n = int(pools[0].head_off[h]), int(pools[0].head_bytes[h])
+            if (b, h) != (2, 3):   # a non-finite q touches only the readout
+                assert np.array_equal(a[off:off + n], c[off:off + n]), f"block of request {b} head {h}"
+    # the head whose readout saw the infinite q still stores the clean block
+    off, n = int(pools[0].head_off[3]), int(pools[0].head_bytes[3])
+    assert np.array_equal(pools[0].qdr_read_raw(int(slot_of[2]))[off:off + n],
+                          pools[1].qdr_read_raw(int(slot_of[2]))[off:off + n])
+    assert not np.all(np.isfinite(outs[1][2, 3]))
+    for p in pools:
+        p.close()

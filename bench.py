@@ -317,6 +317,36 @@ def batch_sweep(cfg, tables, pool, slots, inputs, o, batches=(32, 64, 128, 256),
     return out
 
 
+def clock_under_load(pool, slots, inputs, o, probes: int = 3):
+    """The shader clock (qdr_clock_probe: one wave between two reads of the
+    clock counter and of the 100 MHz counter) while idle, and while decode
+    steps run: the probe goes on a second stream during every tenth-step
+    batch.  A VALU-bound step's time scales with this clock, which the GPU
+    lowers under a heavy load."""
+    import torch
+    from quantized_delta_rule_decode_amd import qdr
+    out = torch.zeros(8, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+
+    def mhz():
+        t0, r0, t1, r1 = (int(x) for x in out[:4].cpu().tolist())
+        return 100.0 * (t1 - t0) / (r1 - r0)
+
+    qdr.qdr_clock_probe(out, 2000, side)
+    torch.cuda.synchronize()
+    idle = mhz()
+    loaded = []
+    for _ in range(probes):
+        for i in range(10):
+            pool.qdr_decode_step(slots, *inputs, o)
+            if i == 3:
+                qdr.qdr_clock_probe(out, 300, side)
+        torch.cuda.synchronize()
+        loaded.append(mhz())
+    return {"idle_MHz": idle, "during_steps_MHz": loaded,
+            "probe": "qdr_clock_probe on a second stream, one wave"}
+
+
 def stream_reference(nbytes: int = 2 << 30, reps: int = 5):
     """HBM rate of a plain in-place streaming kernel on this GPU (torch add_ of
     an fp32 buffer: each byte read once and written once), for scale."""
@@ -393,6 +423,8 @@ def main():
                          "bfloat16-scale pool")
     ap.add_argument("--no-trajectory-error", action="store_true",
                     help="skip the quantised-vs-FP32 trajectory error of the small configs")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip measuring the shader clock while idle and during decode steps")
     ap.add_argument("--no-batch-sweep", action="store_true",
                     help="skip timing the step on the first 32, 64, 128 and 256 requests of the pool")
     ap.add_argument("--no-other-configs", action="store_true",
@@ -482,6 +514,7 @@ def main():
     traj = None if args.no_trajectory_error else \
         [fp32_trajectory_error(1)] + [fp32_trajectory_error(c, f) for c in (2, 3) for f in (0, 1)]
     sweep = None if args.no_batch_sweep else batch_sweep(cfg, tables, pool, slots, (q, k, v, beta, gate), o)
+    clock = None if args.no_clock else clock_under_load(pool, slots, (q, k, v, beta, gate), o)
     assert pool.qdr_poll_device_error() == 0
     others = None if args.no_other_configs else other_configs()
     cpu = None
@@ -543,6 +576,7 @@ def main():
         "bf16_scales_step": sc16,
         "fp32_trajectory_error": traj,
         "batch_sweep": sweep,
+        "shader_clock": clock,
         "other_configs": others,
         "cpu_baseline": cpu,
         "wall_ms_per_step": wall * 1e3 / args.steps,

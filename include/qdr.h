@@ -226,6 +226,16 @@ qdr_status qdr_poll_device_error(qdr_pool *pool, uint32_t *flags);
 /* Message describing the last failed call on this thread ("" if none). */
 const char *qdr_last_error(void);
 
+/* Diagnostic, not part of the decode step: enqueue on `stream` one wave
+ * that runs iters x 256 fma instructions between two reads of the
+ * shader-clock counter and of the constant 100 MHz counter, and stores
+ * out[0..3] = {clock start, 100 MHz start, clock end, 100 MHz end} (out: a
+ * device array of at least 5 uint64; out[4] holds a by-product).  The
+ * shader clock in MHz is 100 (out[2] - out[0]) / (out[3] - out[1]); launched
+ * on a second stream while decode steps run, it gives the clock the steps
+ * run at.  QDR_E_INVAL for a null out or iters <= 0. */
+qdr_status qdr_clock_probe(uint64_t *out, int32_t iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,7 +52,7 @@ class Layout(ctypes.Structure):
 
 EXPORTS = ["qdr_pool_bytes", "qdr_pool_create", "qdr_pool_destroy", "qdr_slot_reset",
            "qdr_pack", "qdr_unpack", "qdr_decode_step", "qdr_decode_step_split", "qdr_decode_step_bf16", "qdr_get_layout", "qdr_read_raw",
-           "qdr_write_raw", "qdr_poll_device_error", "qdr_last_error"]
+           "qdr_write_raw", "qdr_poll_device_error", "qdr_last_error", "qdr_clock_probe"]
 
 _lib = None
 
@@ -84,6 +84,7 @@ def load():
         "qdr_read_raw": [P, I32, P, SZ, P],
         "qdr_write_raw": [P, I32, P, SZ, P],
         "qdr_poll_device_error": [P, ctypes.POINTER(ctypes.c_uint32)],
+        "qdr_clock_probe": [P, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -133,6 +134,16 @@ def qdr_pool_bytes(num_slots, num_heads, kinds, omega, unit=UNIT_HEAD, gate=GATE
     n = ctypes.c_size_t(0)
     _check("qdr_pool_bytes", load().qdr_pool_bytes(ctypes.byref(d), ctypes.byref(n)))
     return int(n.value)
+
+
+def qdr_clock_probe(out, iters, stream=None):
+    """Enqueue the shader-clock probe; out: torch.int64 device tensor of >= 5
+    elements (see include/qdr.h).  Returns nothing; read out after the
+    stream completes: MHz = 100 * (out[2] - out[0]) / (out[3] - out[1])."""
+    import torch
+    if out.numel() < 5:
+        raise ValueError(f"out has {out.numel()} elements, expected at least 5")
+    _check("qdr_clock_probe", load().qdr_clock_probe(_dptr(out, torch.int64, "out"), int(iters), _stream(stream)))
 
 
 class Pool:

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert sorted(names) == sorted(qdr.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n

@@ -77,20 +77,41 @@ def measured_traffic(cid: int, kernel: str | None = None):
     return None if k is None else k["fetch"] + k["write"]
 
 
-def cpu_baseline(cfg, tables, requests: int, threads: int):
-    """The CPU oracle, as it stands, on `requests` requests x all heads."""
+def cpu_baseline(cfg, tables, requests: int, threads: int, compare: bool = False):
+    """The CPU oracle, as it stands, on `requests` requests x all heads.
+    compare: also run the same step (same packed state, same inputs) through
+    the library on a pool of those requests and report how the results agree:
+    blocks byte for byte, the readout at relative L2."""
     from oracle import oracle as orc
     from quantized_delta_rule_decode_amd import synth
     P = orc.Pool(requests, cfg.H, tables["kinds"], tables["omega"], unit=cfg.unit,
                  gate=cfg.gate, scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters).alloc()
     slots = np.arange(requests, dtype=np.int32)
-    P.pack(slots, synth.random_state(77, requests, cfg.H), threads=threads)
+    S = synth.random_state(77, requests, cfg.H)
+    P.pack(slots, S, threads=threads)
     sub = synth.Config(**{**cfg.__dict__, "B": requests, "device_inputs": False})
     ins = synth.step_inputs(sub, tables, 0)
     t0 = time.perf_counter()
-    P.step(slots, *ins, threads=threads)
+    o_ref, _ = P.step(slots, *ins, threads=threads)
     dt = time.perf_counter() - t0
-    return requests * cfg.H / dt, dt
+    parity = None
+    if compare:
+        import torch
+        from quantized_delta_rule_decode_amd import qdr
+        dev = qdr.Pool(requests, cfg.H, tables["kinds"], tables["omega"], unit=cfg.unit, gate=cfg.gate,
+                       scale_mode=cfg.scale_mode, fit_iters=cfg.fit_iters)
+        ds = torch.from_numpy(slots).cuda()
+        dev.qdr_pack(ds, torch.from_numpy(S).cuda())
+        o = torch.empty((requests, cfg.H, 128), dtype=torch.float32, device="cuda")
+        dev.qdr_decode_step(ds, *(torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in ins), o)
+        torch.cuda.synchronize()
+        same = sum(int(np.array_equal(dev.qdr_read_raw(i), P.mem[i * P.slot_stride:(i + 1) * P.slot_stride]))
+                   for i in range(requests))
+        od, orf = o.cpu().numpy().astype(np.float64), np.asarray(o_ref, np.float64)
+        parity = {"requests": requests, "slots_byte_identical": same,
+                  "o_rel_l2": float(np.linalg.norm(od - orf) / np.linalg.norm(orf))}
+        dev.close()
+    return requests * cfg.H / dt, dt, parity
 
 
 def other_configs(cids=(1, 2, 3, 5), reps: int = 20):
@@ -521,11 +542,12 @@ def main():
     if not args.no_cpu_baseline:
         host_cores = os.cpu_count() or 1
         threads = min(host_cores, 16)
-        rate, dt = cpu_baseline(cfg, tables, args.cpu_requests, threads)
-        rate1, dt1 = cpu_baseline(cfg, tables, args.cpu_requests_single, 1)
+        rate, dt, par = cpu_baseline(cfg, tables, args.cpu_requests, threads, compare=True)
+        rate1, dt1, _ = cpu_baseline(cfg, tables, args.cpu_requests_single, 1)
         cpu = {"value": rate, "unit": "state-update steps/s", "cores": threads, "kind": "oracle",
                "sample": f"{args.cpu_requests} requests x {cfg.H} heads, one step ({dt:.2f} s) on {threads} threads",
                "host_cores": host_cores,
+               "parity_with_device": par,
                "single_thread": {"value": rate1, "unit": "state-update steps/s", "cores": 1,
                                  "sample": f"{args.cpu_requests_single} requests x {cfg.H} heads, one step "
                                            f"({dt1:.2f} s)"}}

@@ -568,6 +568,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "inputs": {"tables": f"numpy PCG64, SeedSequence([{cfg.seed} + stream])",
+                   "step_inputs": ("torch Philox on the device, seed "
+                                   f"{cfg.seed} * 100003 + 7919 + step" if cfg.device_inputs
+                                   else f"numpy PCG64, SeedSequence([{cfg.seed} + stream, step])"),
+                   "warm_state": f"{warm} FP32 decode steps from zero, then packed" if warm else "zero state"},
         "config": {"workload": cfg.name, "B": cfg.B, "heads": cfg.H, "d_k": 128, "d_v": 128,
                    "mean_code_bits": round(float(np.mean(tables["kinds"])), 3),
                    "stored_bits_per_value": round(pool.bits_per_value, 3),

@@ -537,18 +537,16 @@ struct Shared : SharedCore {
 // Waves per SIMD the register allocation targets: three for the dual-axis
 // integer kernels (their 128-register tile plus working set fits in 168
 // VGPRs), two where it does not (float kinds, the refit variant, the
-// row-absmax baseline, and the write-back of the two-launch step, which
-// restores the state a second time next to its first readout and spilled
-// over 200 registers at the three-wave budget).
+// row-absmax baseline).
 template <int BITS, int MODE, int SCALE, int FIT>
 struct Occupancy {
-  static constexpr int waves = (BITS <= 8 && FIT == 0 && dual(SCALE) && MODE != MODE_WRITEBACK) ? 3 : 2;
+  static constexpr int waves = (BITS <= 8 && FIT == 0 && dual(SCALE)) ? 3 : 2;
 };
-// The row-unit kernel: three waves per SIMD except the write-back (about 100
-// registers over the three-wave budget) and the pack of dense states (up to 9).
+// The row-unit kernel: three waves per SIMD except the pack of dense states
+// (up to 9 registers over the three-wave budget).
 template <int MODE>
 struct RowsOccupancy {
-  static constexpr int waves = (MODE == MODE_WRITEBACK || MODE == MODE_PACK) ? 2 : 3;
+  static constexpr int waves = (MODE == MODE_PACK) ? 2 : 3;
 };
 
 // The work of one (request b, head h) of kind BITS; sh is the workgroup's
@@ -695,7 +693,8 @@ __device__ __forceinline__ void head_body(const LaunchArgs &P, Shared &sh, const
     __syncthreads();
     float acc2[2] = {0.0f, 0.0f};
     if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
-    chain_rows(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
+    // (the write-back stores no readout: wave 0 skips its S'^T q part)
+    if (!(MODE == MODE_WRITEBACK && w == 0)) chain_rows(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
     if (w == 1) {
       sh.d[l] = sh.d[l] - acc2[0];
       sh.d[l + 64] = sh.d[l + 64] - acc2[1];
@@ -1178,7 +1177,9 @@ k_rows(const LaunchArgs P) {
         }
       }
     }
-    if (has_readout(MODE)) chain_rows_ahead<kAhead>(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
+    // (the write-back stores no readout: wave 1 skips its S'^T q part)
+    if (has_readout(MODE) && !(MODE == MODE_WRITEBACK && w == 1))
+      chain_rows_ahead<kAhead>(S, acc1, (w == 0) ? sh.k : sh.q, 64 * w);
   }
 
   if (MODE == MODE_UNPACK) {
@@ -1213,7 +1214,7 @@ k_rows(const LaunchArgs P) {
     __syncthreads();
     float acc2[2] = {0.0f, 0.0f};
     if (w == 1) { acc2[0] = sh.x[l]; acc2[1] = sh.x[l + 64]; }
-    chain_rows_ahead<kAhead>(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
+    if (!(MODE == MODE_WRITEBACK && w == 0)) chain_rows_ahead<kAhead>(S, acc2, (w == 0) ? sh.q : sh.k, 64 * w);
     if (w == 1) {
       sh.d[l] = sh.d[l] - acc2[0];
       sh.d[l + 64] = sh.d[l + 64] - acc2[1];
